@@ -1,0 +1,122 @@
+/*
+ * fabwd.h - C ABI of the MI355X (gfx950) FlashAttention backward library.
+ *
+ * Sources cited in this header:
+ *   [CB]  Inference Cookbook, "反向传播算法详解" (FlashAttention backward pass
+ *         explained): section 1.2 (recompute P from the saved LSE), 1.3 (what
+ *         the forward saves), 2.1 (the five gradients, dPsum, softcap chain,
+ *         dK scaled by the softmax scale), 3.1 (KV-block-outer loop), 6.2 (dQ
+ *         accumulated with atomics into an fp32 dQaccum buffer), 8.5 (GQA).
+ *   [FA1] "解析 FlashAttention（3）：FlashAttention-v1 反向传播" (FlashAttention-v1
+ *         backward): equations (1)-(16) and Algorithm 4 (section 4).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or synchronises; it only enqueues kernels.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls are asynchronous and ordered only by that stream.  Kernel faults
+ *    surface on a later synchronisation of that stream, as with any launch.
+ *  - Layouts are contiguous row-major with the head dimension d fastest:
+ *      Q, O, dO, dQ : [B, H,    N, d]
+ *      K, V, dK, dV : [B, H_kv, N, d]
+ *      LSE, D       : [B, H, N]       float32
+ *      dQaccum      : [B, H, N, d]    float32
+ *    Element type of Q, K, V, O, dO, dQ, dK, dV is `dtype` (fp32 or bf16).
+ *  - Grouped-query attention: H must be a multiple of H_kv; query head h uses
+ *    key/value head h / (H / H_kv), and dK, dV of a key/value head are the sum
+ *    over its query heads ([CB] 8.5).
+ *  - Scores: R = Q K^T (raw).  With softcap c > 0 the logits are
+ *    Z = scale * c * tanh(R / c), otherwise Z = scale * R ([CB] 2.1: the cap
+ *    acts on the raw scores; the softmax scale multiplies the capped value).
+ *    Causal: key j is masked for query i when j > i (the diagonal is kept).
+ *  - Every pointer must be 16-byte aligned.  Sizes with B*H*N*d beyond
+ *    2^40 elements are rejected.  N = 0 or B = 0 is a valid empty problem:
+ *    the call validates its arguments and enqueues nothing.
+ *  - Return value: ATTN_OK (0) or one of the ATTN_ERR_* codes below.  On an
+ *    error nothing is enqueued.  No exception crosses this interface.
+ */
+#ifndef FABWD_H
+#define FABWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, H % H_kv != 0, scale <= 0, softcap < 0, ... */
+  ATTN_ERR_UNSUPPORTED = 2, /* no kernel instance for this (dtype, d) */
+  ATTN_ERR_MISALIGNED = 3,  /* a pointer is not 16-byte aligned */
+  ATTN_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+};
+
+enum attn_dtype { ATTN_FP32 = 0, ATTN_BF16 = 1 };
+
+typedef struct attn_params {
+  int32_t B, H, H_kv, N, d; /* batch, query heads, key/value heads, sequence length, head dim */
+  int32_t dtype;            /* enum attn_dtype */
+  int32_t causal;           /* 0 or 1 */
+  float scale;              /* softmax scale tau, finite and > 0 (usually 1/sqrt(d)) */
+  float softcap;            /* c > 0 enables the tanh cap, 0 disables it */
+  int32_t deterministic;    /* must be 0: dQ partials are added with fp32 atomics */
+} attn_params;
+
+/* Supported head dimensions: d = 64 and d = 128, for both dtypes. */
+
+/*
+ * attn_fwd_stats - forward pass producing what the backward needs ([CB] 1.3).
+ *   O[b,h,i,:]  = sum_j P_ij V[b,g,j,:],  P_i = softmax_j(Z_ij)   (dtype)
+ *   LSE[b,h,i]  = ln sum_j exp(Z_ij)                             (float32, natural log)
+ * Reads Q, K, V; writes O and LSE.
+ */
+int attn_fwd_stats(const attn_params* p, const void* Q, const void* K, const void* V,
+                   void* O, float* LSE, void* stream);
+
+/*
+ * attn_bwd_preprocess - D = rowsum(dO o O) ([FA1] eq (6); [CB] 2.1 dPsum),
+ * accumulated in float32, and dQaccum <- 0.
+ * Reads O, dO; writes D [B,H,N] and zeroes dQaccum [B,H,N,d].
+ */
+int attn_bwd_preprocess(const attn_params* p, const void* O, const void* dO,
+                        float* D, float* dQaccum, void* stream);
+
+/*
+ * attn_bwd - the recompute-based backward ([FA1] Algorithm 4; [CB] 3.1, 5.2).
+ * For every key/value block j (outer) and query block i (inner):
+ *   P   = exp(Z - LSE)                ([CB] 1.2)
+ *   dV += P^T dO                      ([FA1] eq (10))
+ *   dP  = dO V^T                      ([FA1] eq (11))
+ *   dS  = P o (dP - D), times (1 - tanh^2(R/c)) with a cap   ([FA1] eq (14); [CB] 2.1)
+ *   dK += dS^T Q, scaled by `scale` once at the end            ([FA1] eq (16); [CB] 2.1)
+ *   dQaccum += dS K (unscaled; fp32 atomics, [CB] 6.2)         ([FA1] eq (15))
+ * Inputs: Q, K, V, dO (dtype), LSE from attn_fwd_stats, D from
+ * attn_bwd_preprocess.  dQaccum must have been zeroed by attn_bwd_preprocess
+ * on the same stream.  dK and dV are overwritten (not accumulated into).
+ * dQaccum receives sum_j dS_ij K_j without the scale; attn_bwd_dq_convert
+ * applies it.  The order of the fp32 additions into dQaccum is not fixed, so
+ * its low bits may differ between runs.
+ */
+int attn_bwd(const attn_params* p, const void* Q, const void* K, const void* V,
+             const void* dO, const float* LSE, const float* D,
+             float* dQaccum, void* dK, void* dV, void* stream);
+
+/*
+ * attn_bwd_dq_convert - dQ = scale * dQaccum, rounded to dtype
+ * (round-to-nearest-even for bf16) ([FA1] eq (7): dQ carries the scale).
+ */
+int attn_bwd_dq_convert(const attn_params* p, const float* dQaccum, void* dQ, void* stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* attn_status_str(int status);
+
+/* Library version string (static storage). */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FABWD_H */
