@@ -1,0 +1,18 @@
+// Chooses the kernel family for each entry point.
+#include "fabwd_launch.h"
+
+namespace fabwd {
+
+hipError_t launch_fwd_stats(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            hipStream_t s) {
+  (void)hipGetLastError();
+  return launch_fwd_simple(p, Q, K, V, O, LSE, s);
+}
+
+hipError_t launch_bwd(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                      const float* LSE, const float* D, float* dQacc, void* dK, void* dV, hipStream_t s) {
+  (void)hipGetLastError();
+  return launch_bwd_simple(p, Q, K, V, dO, LSE, D, dQacc, dK, dV, s);
+}
+
+}  // namespace fabwd

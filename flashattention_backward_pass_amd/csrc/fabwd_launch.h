@@ -1,0 +1,36 @@
+// Host-side launchers of the gfx950 kernels.  The C ABI (api.cpp) validates
+// arguments and then calls exactly one launcher per entry point.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fabwd {
+
+// Problem description shared by the launchers (already validated).
+struct Problem {
+  int B, H, H_kv, N, d;
+  int dtype;  // 0 fp32, 1 bf16
+  bool causal;
+  float scale;
+  float softcap;
+  int group() const { return H / H_kv; }
+  int64_t q_rows() const { return int64_t(B) * H * N; }
+  int64_t q_elems() const { return q_rows() * d; }
+};
+
+hipError_t launch_fwd_stats(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            hipStream_t s);
+hipError_t launch_bwd_preprocess(const Problem& p, const void* O, const void* dO, float* D, float* dQacc,
+                                 hipStream_t s);
+hipError_t launch_bwd(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                      const float* LSE, const float* D, float* dQacc, void* dK, void* dV, hipStream_t s);
+hipError_t launch_bwd_dq_convert(const Problem& p, const float* dQacc, void* dQ, hipStream_t s);
+
+// Kernel families behind launch_fwd_stats / launch_bwd (dispatch.cpp picks one).
+hipError_t launch_fwd_simple(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                             hipStream_t s);
+hipError_t launch_bwd_simple(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                             const float* LSE, const float* D, float* dQacc, void* dK, void* dV, hipStream_t s);
+
+}  // namespace fabwd

@@ -1,0 +1,283 @@
+// Vector-ALU (fp32 FMA) forward and backward kernels.
+//
+// These serve the fp32 workloads (on MI355X the fp32 vector and fp32 matrix
+// peaks are the same, 157.3 TFLOP/s) and any configuration the bf16 MFMA
+// kernels do not cover.  They follow the tiling of
+// "解析 FlashAttention（3）：FlashAttention-v1 反向传播", section 4 (Algorithm 4):
+// key/value blocks outer, query blocks inner, P recomputed per tile from the
+// saved LSE (Inference Cookbook "反向传播算法详解", section 1.2), dK and dV kept
+// on chip, dQ partials added into an fp32 buffer (section 6.2 of the latter).
+//
+// Arithmetic: inputs are widened to fp32, every product and sum is fp32, and
+// exponentials are hardware exp2 with the log2(e) factor folded into the
+// scale.  The forward is the online-softmax loop of the Cookbook page,
+// section 3.1 (query blocks outer, key blocks inner).
+#include "fabwd_device.h"
+#include "fabwd_launch.h"
+
+namespace fabwd {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// ----------------------------------------------------------------- forward
+// One workgroup per (query block of 32 rows, head, batch); 8 lanes per row.
+template <typename T, int D, bool CAUSAL, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads) void fwd_simple_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                              const T* __restrict__ V, T* __restrict__ O,
+                                                              float* __restrict__ LSE, int H, int H_kv, int N,
+                                                              float scale, float softcap) {
+  constexpr int BQ = 32, BK = 64, DX = D / 8;
+  __shared__ float sQ[BQ][D];
+  __shared__ float sK[BK][D + 1];
+  __shared__ float sV[BK][D];
+  __shared__ float sP[BQ][BK + 1];
+
+  const int t = threadIdx.x, r = t >> 3, sub = t & 7;
+  const int q0 = blockIdx.x * BQ, h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / (H / H_kv);
+  const T* q_base = Q + (int64_t(b) * H + h) * N * D;
+  const T* k_base = K + (int64_t(b) * H_kv + hk) * N * D;
+  const T* v_base = V + (int64_t(b) * H_kv + hk) * N * D;
+
+  for (int idx = t; idx < BQ * D; idx += kThreads) {
+    const int rr = idx / D, x = idx % D;
+    sQ[rr][x] = (q0 + rr < N) ? Elem<T>::load(q_base, int64_t(q0 + rr) * D + x) : 0.f;
+  }
+  const int row = q0 + r;
+  float m_run = -INFINITY, l_run = 0.f;
+  float acc[DX];
+#pragma unroll
+  for (int k = 0; k < DX; ++k) acc[k] = 0.f;
+
+  const int kv_end = CAUSAL ? min(N, q0 + BQ) : N;
+  const float zscale = scale * kLog2e;
+  for (int k0 = 0; k0 < kv_end; k0 += BK) {
+    __syncthreads();
+    for (int idx = t; idx < BK * D; idx += kThreads) {
+      const int kk = idx / D, x = idx % D;
+      const bool ok = k0 + kk < N;
+      sK[kk][x] = ok ? Elem<T>::load(k_base, int64_t(k0 + kk) * D + x) : 0.f;
+      sV[kk][x] = ok ? Elem<T>::load(v_base, int64_t(k0 + kk) * D + x) : 0.f;
+    }
+    __syncthreads();
+    float z[BK / 8];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < BK / 8; ++m) {
+      const int c = sub + 8 * m, key = k0 + c;
+      float s = 0.f;
+#pragma unroll 8
+      for (int x = 0; x < D; ++x) s = fmaf(sQ[r][x], sK[c][x], s);
+      if (SOFTCAP) s = softcap * tanh_f32(s / softcap);
+      float zz = s * zscale;
+      if (key >= N || (CAUSAL && key > row)) zz = -INFINITY;
+      z[m] = zz;
+      bmax = fmaxf(bmax, zz);
+    }
+    bmax = wave_xor_max(bmax, 8);
+    const float m_new = fmaxf(m_run, bmax);
+    const float base = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - base);
+    float psum = 0.f;
+#pragma unroll
+    for (int m = 0; m < BK / 8; ++m) {
+      const float p = fast_exp2(z[m] - base);
+      psum += p;
+      sP[r][sub + 8 * m] = p;
+    }
+    psum = wave_xor_sum(psum, 8);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < DX; ++k) {
+      const int x = sub + 8 * k;
+      float a = acc[k] * alpha;
+      for (int c = 0; c < BK; ++c) a = fmaf(sP[r][c], sV[c][x], a);
+      acc[k] = a;
+    }
+  }
+  if (row < N) {
+    const float inv_l = 1.0f / l_run;
+    T* o_row = O + ((int64_t(b) * H + h) * N + row) * D;
+#pragma unroll
+    for (int k = 0; k < DX; ++k) Elem<T>::store(o_row, sub + 8 * k, acc[k] * inv_l);
+    if (sub == 0) LSE[(int64_t(b) * H + h) * N + row] = (m_run + __log2f(l_run)) * kLn2;
+  }
+}
+
+// ----------------------------------------------------------------- backward
+// One workgroup per (key block of 32 keys, key/value head, batch); it loops
+// over the query heads of its group and over query blocks of 32 rows.
+template <typename T, int D, bool CAUSAL, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads) void bwd_simple_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                              const T* __restrict__ V, const T* __restrict__ dO,
+                                                              const float* __restrict__ LSE,
+                                                              const float* __restrict__ Dv,
+                                                              float* __restrict__ dQacc, T* __restrict__ dK,
+                                                              T* __restrict__ dV, int H, int H_kv, int N,
+                                                              float scale, float softcap) {
+  constexpr int BK = 32, BQ = 32, DX = D / 8;
+  __shared__ float sK[BK][D + 1];
+  __shared__ float sV[BK][D + 1];
+  __shared__ float sQ[BQ][D + 1];
+  __shared__ float sdO[BQ][D + 1];
+  __shared__ float sP[BQ][BK + 1];
+  __shared__ float sdS[BQ][BK + 1];
+  __shared__ float sL[BQ];
+  __shared__ float sD[BQ];
+
+  const int t = threadIdx.x, r = t >> 3, sub = t & 7;
+  const int k0 = blockIdx.x * BK, hk = blockIdx.y, b = blockIdx.z;
+  const int G = H / H_kv;
+  const int64_t kv_off = (int64_t(b) * H_kv + hk) * N * D;
+
+  for (int idx = t; idx < BK * D; idx += kThreads) {
+    const int kk = idx / D, x = idx % D;
+    const bool ok = k0 + kk < N;
+    sK[kk][x] = ok ? Elem<T>::load(K + kv_off, int64_t(k0 + kk) * D + x) : 0.f;
+    sV[kk][x] = ok ? Elem<T>::load(V + kv_off, int64_t(k0 + kk) * D + x) : 0.f;
+  }
+  float acc_dk[DX], acc_dv[DX];
+#pragma unroll
+  for (int k = 0; k < DX; ++k) acc_dk[k] = acc_dv[k] = 0.f;
+
+  const float zscale = scale * kLog2e;
+  const int q_begin = CAUSAL ? (k0 / BQ) * BQ : 0;
+  for (int hg = 0; hg < G; ++hg) {
+    const int h = hk * G + hg;
+    const int64_t q_off = (int64_t(b) * H + h) * N;
+    for (int q0 = q_begin; q0 < N; q0 += BQ) {
+      __syncthreads();
+      for (int idx = t; idx < BQ * D; idx += kThreads) {
+        const int rr = idx / D, x = idx % D;
+        const bool ok = q0 + rr < N;
+        sQ[rr][x] = ok ? Elem<T>::load(Q, (q_off + q0 + rr) * D + x) : 0.f;
+        sdO[rr][x] = ok ? Elem<T>::load(dO, (q_off + q0 + rr) * D + x) : 0.f;
+      }
+      if (t < BQ) {
+        const bool ok = q0 + t < N;
+        sL[t] = ok ? LSE[q_off + q0 + t] * kLog2e : INFINITY;
+        sD[t] = ok ? Dv[q_off + q0 + t] : 0.f;
+      }
+      __syncthreads();
+      const int row = q0 + r;
+#pragma unroll
+      for (int m = 0; m < BK / 8; ++m) {
+        const int c = sub + 8 * m, key = k0 + c;
+        float s = 0.f, dp = 0.f;
+#pragma unroll 8
+        for (int x = 0; x < D; ++x) {
+          s = fmaf(sQ[r][x], sK[c][x], s);
+          dp = fmaf(sdO[r][x], sV[c][x], dp);
+        }
+        float dtanh = 1.f;
+        if (SOFTCAP) {
+          const float th = tanh_f32(s / softcap);
+          s = softcap * th;
+          dtanh = 1.f - th * th;
+        }
+        const bool masked = key >= N || row >= N || (CAUSAL && key > row);
+        const float p = masked ? 0.f : fast_exp2(s * zscale - sL[r]);
+        sP[r][c] = p;
+        sdS[r][c] = p * (dp - sD[r]) * dtanh;
+      }
+      __syncthreads();
+      // dV += P^T dO and dK += dS^T Q for key r (this thread's key row).
+#pragma unroll
+      for (int k = 0; k < DX; ++k) {
+        const int x = sub + 8 * k;
+        float av = acc_dv[k], ak = acc_dk[k];
+        for (int rr = 0; rr < BQ; ++rr) {
+          av = fmaf(sP[rr][r], sdO[rr][x], av);
+          ak = fmaf(sdS[rr][r], sQ[rr][x], ak);
+        }
+        acc_dv[k] = av;
+        acc_dk[k] = ak;
+      }
+      // dQ partial of this (query block, key block) pair, unscaled.
+      if (row < N) {
+#pragma unroll
+        for (int k = 0; k < DX; ++k) {
+          const int x = sub + 8 * k;
+          float a = 0.f;
+          for (int c = 0; c < BK; ++c) a = fmaf(sdS[r][c], sK[c][x], a);
+          atomic_add_f32(dQacc + (q_off + row) * D + x, a);
+        }
+      }
+    }
+  }
+  const int key = k0 + r;
+  if (key < N) {
+#pragma unroll
+    for (int k = 0; k < DX; ++k) {
+      const int x = sub + 8 * k;
+      Elem<T>::store(dK + kv_off, int64_t(key) * D + x, acc_dk[k] * scale);
+      Elem<T>::store(dV + kv_off, int64_t(key) * D + x, acc_dv[k]);
+    }
+  }
+}
+
+template <typename T, int D, bool C, bool S>
+hipError_t fwd_simple_t(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                        hipStream_t s) {
+  dim3 grid((p.N + 31) / 32, p.H, p.B);
+  hipLaunchKernelGGL((fwd_simple_kernel<T, D, C, S>), grid, dim3(kThreads), 0, s, static_cast<const T*>(Q),
+                     static_cast<const T*>(K), static_cast<const T*>(V), static_cast<T*>(O), LSE, p.H, p.H_kv,
+                     p.N, p.scale, p.softcap);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool C, bool S>
+hipError_t bwd_simple_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                        const float* LSE, const float* Dv, float* dQacc, void* dK, void* dV, hipStream_t s) {
+  dim3 grid((p.N + 31) / 32, p.H_kv, p.B);
+  hipLaunchKernelGGL((bwd_simple_kernel<T, D, C, S>), grid, dim3(kThreads), 0, s, static_cast<const T*>(Q),
+                     static_cast<const T*>(K), static_cast<const T*>(V), static_cast<const T*>(dO), LSE, Dv,
+                     dQacc, static_cast<T*>(dK), static_cast<T*>(dV), p.H, p.H_kv, p.N, p.scale, p.softcap);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t fwd_simple_d(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                        hipStream_t s) {
+  const bool sc = p.softcap > 0.f;
+  if (p.causal) return sc ? fwd_simple_t<T, D, true, true>(p, Q, K, V, O, LSE, s)
+                          : fwd_simple_t<T, D, true, false>(p, Q, K, V, O, LSE, s);
+  return sc ? fwd_simple_t<T, D, false, true>(p, Q, K, V, O, LSE, s)
+            : fwd_simple_t<T, D, false, false>(p, Q, K, V, O, LSE, s);
+}
+
+template <typename T, int D>
+hipError_t bwd_simple_d(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                        const float* LSE, const float* Dv, float* dQacc, void* dK, void* dV, hipStream_t s) {
+  const bool sc = p.softcap > 0.f;
+  if (p.causal) return sc ? bwd_simple_t<T, D, true, true>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s)
+                          : bwd_simple_t<T, D, true, false>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s);
+  return sc ? bwd_simple_t<T, D, false, true>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s)
+            : bwd_simple_t<T, D, false, false>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_simple(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                             hipStream_t s) {
+  if (p.dtype == 1)
+    return p.d == 64 ? fwd_simple_d<bf16_t, 64>(p, Q, K, V, O, LSE, s)
+                     : fwd_simple_d<bf16_t, 128>(p, Q, K, V, O, LSE, s);
+  return p.d == 64 ? fwd_simple_d<float, 64>(p, Q, K, V, O, LSE, s)
+                   : fwd_simple_d<float, 128>(p, Q, K, V, O, LSE, s);
+}
+
+hipError_t launch_bwd_simple(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                             const float* LSE, const float* Dv, float* dQacc, void* dK, void* dV, hipStream_t s) {
+  if (p.dtype == 1)
+    return p.d == 64 ? bwd_simple_d<bf16_t, 64>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s)
+                     : bwd_simple_d<bf16_t, 128>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s);
+  return p.d == 64 ? bwd_simple_d<float, 64>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s)
+                   : bwd_simple_d<float, 128>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s);
+}
+
+}  // namespace fabwd

@@ -1,0 +1,132 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call.
+
+No test here launches a kernel: every call either fails validation or is an
+empty problem (which enqueues nothing).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import flashattention_backward_pass_amd as fab
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fabwd.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fab.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return fab.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for n in ("attn_fwd_stats", "attn_bwd_preprocess", "attn_bwd", "attn_bwd_dq_convert", "attn_status_str"):
+        assert n in names
+
+
+def test_library_exports_every_header_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), f"libfabwd.so does not export {name}"
+    assert set(header_functions()) == set(fab.EXPORTS), "binding table out of sync with the header"
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        s = fab.status_str(code)
+        assert s.startswith("ATTN_")
+    assert "unknown" in fab.status_str(99)
+    assert lib.attn_version().decode().startswith("fabwd")
+
+
+def test_params_layout_matches_header():
+    # 7 int32 + 2 float + 1 int32, no padding
+    assert ctypes.sizeof(fab.attn_params) == 40
+
+
+# Fake, 16-byte aligned, non-null device pointers: validation rejects the call
+# before they could be used.
+A = ctypes.c_void_p(0x10000)
+MIS = ctypes.c_void_p(0x10008)
+S = ctypes.c_void_p(0)
+
+
+def call_all(lib, p, ptr=A):
+    pp = ctypes.byref(p)
+    return [
+        lib.attn_fwd_stats(pp, ptr, ptr, ptr, ptr, ptr, S),
+        lib.attn_bwd_preprocess(pp, ptr, ptr, ptr, ptr, S),
+        lib.attn_bwd(pp, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, S),
+        lib.attn_bwd_dq_convert(pp, ptr, ptr, S),
+    ]
+
+
+BAD = [
+    dict(H=0), dict(H_kv=0), dict(H=6, H_kv=4), dict(N=-1), dict(B=-2), dict(d=0), dict(dtype=2),
+    dict(causal=2), dict(scale=0.0), dict(scale=-1.0), dict(scale=float("nan")), dict(scale=float("inf")),
+    dict(softcap=-1.0), dict(softcap=float("inf")), dict(N=(1 << 24) + 1),
+]
+
+
+@pytest.mark.parametrize("bad", BAD, ids=[str(b) for b in BAD])
+def test_invalid_arguments(lib, bad):
+    kw = dict(B=1, H=4, H_kv=2, N=64, d=64, dtype=1, causal=0, scale=0.125, softcap=0.0)
+    kw.update(bad)
+    p = fab.attn_params(kw["B"], kw["H"], kw["H_kv"], kw["N"], kw["d"], kw["dtype"], kw["causal"], kw["scale"],
+                        kw["softcap"], 0)
+    assert call_all(lib, p) == [fab.ATTN_ERR_INVALID_ARG] * 4
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_unsupported_head_dim(lib, d):
+    assert call_all(lib, fab.make_params(1, 2, 2, 64, d, 1)) == [fab.ATTN_ERR_UNSUPPORTED] * 4
+
+
+def test_deterministic_mode_unsupported(lib):
+    assert call_all(lib, fab.make_params(1, 2, 2, 64, 64, 1, deterministic=1)) == [fab.ATTN_ERR_UNSUPPORTED] * 4
+
+
+def test_null_params(lib):
+    assert lib.attn_bwd_dq_convert(None, A, A, S) == fab.ATTN_ERR_INVALID_ARG
+
+
+def test_null_pointers(lib):
+    assert call_all(lib, fab.make_params(1, 2, 2, 64, 64, 1), ptr=ctypes.c_void_p(0)) == \
+        [fab.ATTN_ERR_INVALID_ARG] * 4
+
+
+def test_misaligned_pointers(lib):
+    assert call_all(lib, fab.make_params(1, 2, 2, 64, 64, 1), ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * 4
+
+
+def test_too_many_elements(lib):
+    assert call_all(lib, fab.make_params(1 << 12, 1 << 10, 1, 1 << 13, 128, 1)) == [fab.ATTN_ERR_INVALID_ARG] * 4
+
+
+@pytest.mark.parametrize("shape", [(0, 2, 2, 64), (1, 2, 2, 0)])
+def test_empty_problems_are_ok_without_pointers(lib, shape):
+    B, H, Hkv, N = shape
+    assert call_all(lib, fab.make_params(B, H, Hkv, N, 128, 1, causal=1), ptr=ctypes.c_void_p(0)) == \
+        [fab.ATTN_OK] * 4
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    saved = fab._lib
+    try:
+        fab._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            fab.load_library(str(tmp_path / "missing.so"))
+    finally:
+        fab._lib = saved
