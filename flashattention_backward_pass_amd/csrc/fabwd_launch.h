@@ -32,5 +32,7 @@ hipError_t launch_fwd_simple(const Problem& p, const void* Q, const void* K, con
                              hipStream_t s);
 hipError_t launch_bwd_simple(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                              const float* LSE, const float* D, float* dQacc, void* dK, void* dV, hipStream_t s);
+hipError_t launch_bwd_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                           const float* LSE, const float* D, float* dQacc, void* dK, void* dV, hipStream_t s);
 
 }  // namespace fabwd
