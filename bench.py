@@ -1,0 +1,199 @@
+"""Benchmark of the attention backward hot path on one MI355X.
+
+One step = attn_bwd_preprocess (D = rowsum(dO o O), dQaccum <- 0) + attn_bwd +
+attn_bwd_dq_convert on the long-sequence causal workload (B=1, H=8, N=16384,
+d=128, bf16), with Q, K, V, dO, O and LSE resident in HBM before the timed
+region (O and LSE come from attn_fwd_stats, outside the timed region).
+
+Throughput: backward FLOPs of the metric, 10 N^2 d per query head, halved for
+a causal mask, divided by the measured time per step.  Prints one JSON line.
+
+Flags: --gpus N (only 1 is supported: the library and this run use one GPU),
+--steps K, --warmup W, --workload NAME, --no-cpu-baseline,
+--copy-calibration (time a plain 1 GiB device copy instead; its known byte
+count calibrates the FETCH_SIZE / WRITE_SIZE counters of rocprofv3).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention-backward TFLOP/s (10·N²·d/head) and % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "bf16_causal_b1h8_n16384_d128"
+BWD_SOURCE = os.path.join(ROOT, "flashattention_backward_pass_amd", "csrc", "bwd_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_mfma_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    return ap.parse_args()
+
+
+def source_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(launch_bytes_key="bytes_per_launch"):
+    """HBM bytes per attn_bwd launch from committed rocprofv3 counter runs,
+    valid only while the kernel source is the one the counters were taken on."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != source_sha(BWD_SOURCE):
+        return None
+    return t.get(launch_bytes_key)
+
+
+def copy_calibration(torch):
+    n = 1 << 28  # 2^28 float32 = 1 GiB
+    src = torch.ones(n, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 10
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "ms": dt * 1e3,
+                      "GBs": 2 * n * 4 / dt / 1e9}), flush=True)
+
+
+def cpu_baseline(w, x):
+    """The fp64 oracle, untuned, on one query head of the workload at full N."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    q, k, v, do = (x[n][0, 0] for n in ("Q", "K", "V", "dO"))
+    t0 = time.perf_counter()
+    O, L = oracle.forward_head(q, k, v, w.tau, w.causal, w.softcap)
+    oracle.backward_head(q, k, v, O, do, L, w.tau, w.causal, w.softcap)
+    dt = time.perf_counter() - t0
+    flops = 10.0 * w.N * w.N * w.d / (2.0 if w.causal else 1.0)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"one query head (b=0, h=0) of the workload at full N={w.N}: fp64 forward + backward, "
+                      f"{dt:.1f} s wall; metric FLOPs of that head",
+            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the backward library is a "
+              "single-GPU path; see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import flashattention_backward_pass_amd as fab
+    from flashattention_backward_pass_amd import workloads
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    w = workloads.WORKLOADS[args.workload]
+    fab.load_library()
+    x = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x[n].to(dev) for n in ("Q", "K", "V", "dO"))
+    kw = dict(causal=w.causal, scale=w.tau, softcap=w.softcap)
+    o, lse = fab.attention_forward(q, k, v, **kw)
+    B, H, N, d = q.shape
+    D = torch.empty(B, H, N, device=dev, dtype=torch.float32)
+    acc = torch.empty(B, H, N, d, device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fab.attn_bwd_preprocess(o, do, D, acc, H_kv=w.H_kv, **kw)
+        if ev is not None:
+            ev[1].record()
+        fab.attn_bwd(q, k, v, do, lse, D, acc, dk, dv, **kw)
+        if ev is not None:
+            ev[2].record()
+        fab.attn_bwd_dq_convert(acc, dq, scale=w.tau)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # Timed region: exactly K steps, synchronised on both sides.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    cvt = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    flops = w.flops()
+    ms = wall / args.steps * 1e3
+    value = flops / (ms * 1e-3) / 1e12
+    bwd_tflops = flops / (bwd * 1e-3) / 1e12
+    esz = 2 if w.dtype == "bf16" else 4
+    pre_bytes = 2 * B * H * N * d * esz + B * H * N * 4           # read O, dO; write D
+    cvt_bytes = B * H * N * d * 4 + B * H * N * d * esz           # read dQaccum; write dQ
+    traffic = measured_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded iid normal Q, K, V, dO; O and LSE from attn_fwd_stats)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "softcap": w.softcap, "tau": w.tau, "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(bwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "attn_bwd (bwd_mfma_kernel)", "flops_per_launch": flops},
+        "kernels_ms": {"bwd_preprocess": round(pre, 4), "bwd": round(bwd, 4), "bwd_dq_convert": round(cvt, 4)},
+        "stream_kernels_GBs": {"bwd_preprocess": round(pre_bytes / (pre * 1e-3) / 1e9, 1),
+                               "bwd_dq_convert": round(cvt_bytes / (cvt * 1e-3) / 1e9, 1),
+                               "peak": PEAK_HBM_GBS},
+    }
+    try:
+        out["git"] = subprocess.run(["git", "rev-parse", "--short", "HEAD"], capture_output=True, text=True,
+                                    cwd=ROOT).stdout.strip() or None
+    except Exception:
+        out["git"] = None
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
