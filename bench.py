@@ -30,8 +30,9 @@ METRIC = "attention-backward TFLOP/s (10·N²·d/head) and % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 DEFAULT_WORKLOAD = "bf16_causal_b1h8_n16384_d128"
-BWD_SOURCE = os.path.join(ROOT, "flashattention_backward_pass_amd", "csrc", "bwd_mfma.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_mfma_traffic.json")
+BWD_SOURCES = [os.path.join(ROOT, "flashattention_backward_pass_amd", "csrc", f)
+               for f in ("bwd_dkdv.hip", "bwd_dq.hip", "mfma_common.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_traffic.json")
 
 
 def parse():
@@ -45,8 +46,11 @@ def parse():
     return ap.parse_args()
 
 
-def source_sha(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(launch_bytes_key="bytes_per_launch"):
@@ -56,7 +60,7 @@ def measured_traffic(launch_bytes_key="bytes_per_launch"):
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != source_sha(BWD_SOURCE):
+    if t.get("source_sha") != source_sha(BWD_SOURCES):
         return None
     return t.get(launch_bytes_key)
 
@@ -179,7 +183,11 @@ def main():
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(bwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "attn_bwd (bwd_mfma_kernel)", "flops_per_launch": flops},
+                     "kernel": "attn_bwd entry point (bf16: bwd_dkdv_kernel + bwd_dq_kernel)",
+                     "flops_per_launch": flops,
+                     "note": "achieved = metric FLOPs (10 N^2 d per head, halved when causal) / measured attn_bwd "
+                             "time; the two kernels issue 14 N^2 d (halved) of MFMA work because the dQ kernel "
+                             "recomputes S and dP"},
         "kernels_ms": {"bwd_preprocess": round(pre, 4), "bwd": round(bwd, 4), "bwd_dq_convert": round(cvt, 4)},
         "stream_kernels_GBs": {"bwd_preprocess": round(pre_bytes / (pre * 1e-3) / 1e9, 1),
                                "bwd_dq_convert": round(cvt_bytes / (cvt * 1e-3) / 1e9, 1),

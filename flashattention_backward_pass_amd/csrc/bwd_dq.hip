@@ -1,0 +1,185 @@
+// bf16 dQ kernel on gfx950 matrix cores: query blocks outer, key blocks inner.
+//
+// dQ_i = sum_j dS_ij K_j ("解析 FlashAttention（3）：FlashAttention-v1 反向传播",
+// eq (15), without the scale tau, which the convert kernel applies).  The
+// pages accumulate dQ across key blocks with fp32 atomics into a global
+// buffer (Inference Cookbook "反向传播算法详解", section 6.2).  On MI355X every
+// global float atomic is executed at the memory side rather than in L2, which
+// caps that path near 1.3 TB/s of update traffic; this kernel instead gives
+// each workgroup a whole block of query rows, recomputes S and dP for them
+// (P from the saved LSE, section 1.2 of the Cookbook page), and keeps dQ in
+// registers over all key blocks, so dQaccum is written once with plain
+// stores and the result does not depend on any summation order across
+// workgroups.
+//
+// Per workgroup: 128 query rows of one query head (wave w owns rows
+// 32w..32w+31), key blocks of 64 streamed through double-buffered LDS tiles.
+// Per key block and 32-key half:
+//   S^T  = K Q^T      (keys x queries; Q rows of this wave in registers)
+//   dP^T = V dO^T
+//   P = exp2(S' tau log2e - LSE log2e), dS = P o (dP - D) [o (1 - tanh^2)]
+//   dQ  += dS K       (dS^T accumulator layout = A operand with queries on
+//                      lanes; K^T read transposed from the row-major K tile)
+// Computing S^T rather than S puts one query per lane, so LSE and D are one
+// register each.
+#include "fabwd_launch.h"
+#include "mfma_common.h"
+
+namespace fabwd {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int BQ = 128;  // query rows per workgroup
+constexpr int BK = 64;   // keys per inner step
+
+template <int D, bool CAUSAL, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
+    float* __restrict__ dQacc, int H, int H_kv, int N, int BHq, float scale, float softcap) {
+  constexpr int KC = D / 16;
+  constexpr int NT = D / 32;
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][BK * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int j16 = lane & 15, h16 = (lane >> 4) & 1;
+
+  // Work unit: (batch*query head, query block); query blocks vary slowest,
+  // last (heaviest under a causal mask) first.
+  const int n_qblk = (N + BQ - 1) / BQ;
+  const int bhq = blockIdx.x % BHq;
+  const int iblk = n_qblk - 1 - int(blockIdx.x / BHq);
+  const int b = bhq / H, h = bhq % H;
+  const int hk = h / (H / H_kv);
+  const int q0 = iblk * BQ;
+  const int64_t q_off = (int64_t(b) * H + h) * N;
+  const int64_t kv_off = (int64_t(b) * H_kv + hk) * N;
+  const int my_q = q0 + 32 * w + l32;  // query row owned by this lane
+  const int my_qc = min(my_q, N - 1);
+
+  // Q and dO rows of this lane (B operands of S^T and dP^T), LSE and D.
+  bf16x8_t qreg[KC], doreg[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    qreg[c] = load_bf16x8(Q + (q_off + my_qc) * D + 16 * c + 8 * g);
+    doreg[c] = load_bf16x8(dO + (q_off + my_qc) * D + 16 * c + 8 * g);
+  }
+  const float nl2 = -LSE[q_off + my_qc] * kLog2e;
+  const float dval = Dv[q_off + my_qc];
+  const float zs = scale * kLog2e;
+
+  f32x16_t dq_acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) dq_acc[n] = f32x16_t{};
+
+  const int kv_end = CAUSAL ? min(N, q0 + BQ) : N;
+  const int n_steps = (kv_end + BK - 1) / BK;
+
+  auto issue = [&](int step) {
+    const int kb = step * BK;
+    dma_tile<D, BK>(K + (kv_off + kb) * D, N - kb, sK[step & 1], lane, w);
+    dma_tile<D, BK>(V + (kv_off + kb) * D, N - kb, sV[step & 1], lane, w);
+  };
+
+  issue(0);
+  for (int step = 0; step < n_steps; ++step) {
+    const int buf = step & 1;
+    const int kb = step * BK;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // block `step` in LDS; buffer (step+1)%2 no longer read
+    if (step + 1 < n_steps) issue(step + 1);
+    const bool masked = (CAUSAL && kb + BK > q0) || kb + BK > N;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      // S^T, dP^T for keys kb + 32 s .. + 31 (rows) x this wave's 32 queries (columns).
+      f32x16_t st = {}, dpt = {};
+      const int row = 32 * s + l32;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const int off = swz_off<D>(row, 2 * c + g, 0);
+        st = mfma32(*reinterpret_cast<const bf16x8_t*>(&sK[buf][off]), qreg[c], st);
+        dpt = mfma32(*reinterpret_cast<const bf16x8_t*>(&sV[buf][off]), doreg[c], dpt);
+      }
+      // Register r: key kb + 32 s + 8(r/4) + 4g + r%4, query my_q.
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = st[r];
+        float dt = 1.f;
+        if (SOFTCAP) {
+          const float th = tanh_f32(x / softcap);
+          x = softcap * th;
+          dt = 1.f - th * th;
+        }
+        float p = fast_exp2(fmaf(x, zs, nl2));
+        if (masked) {
+          const int key = kb + 32 * s + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= N || (CAUSAL && key > my_q)) p = 0.f;
+        }
+        float ds = p * (dpt[r] - dval);
+        if (SOFTCAP) ds *= dt;
+        st[r] = ds;
+      }
+      bf16x8_t dsf[2];
+      dsf[0] = pack_bf16x8(st, 0);
+      dsf[1] = pack_bf16x8(st, 8);
+      // dQ += dS K over these 32 keys: K operand rows 32 s + 16u + 4g + (0..3) and +8.
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const int ch = 4 * n + 2 * h16 + ((j16 & 3) >> 1);
+        const int sub = 4 * (j16 & 1);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int r0 = 32 * s + 16 * u + 4 * g + (j16 >> 2);
+          const bf16x8_t kop = cat8(lds_read_tr(&sK[buf][swz_off<D>(r0, ch, sub)]),
+                                    lds_read_tr(&sK[buf][swz_off<D>(r0 + 8, ch, sub)]));
+          dq_acc[n] = mfma32(dsf[u], kop, dq_acc[n]);
+        }
+      }
+    }
+  }
+
+  // dQaccum rows of this wave (unscaled).  Register r: row 32w + 8(r/4) + 4g + r%4.
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int q = q0 + 32 * w + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (q < N) dQacc[(q_off + q) * D + 32 * n + l32] = dq_acc[n][r];
+    }
+  }
+}
+
+template <int D, bool CAUSAL, bool SOFTCAP>
+hipError_t dq_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                const float* Dv, float* dQacc, hipStream_t s) {
+  const int BHq = p.B * p.H;
+  const int n_qblk = (p.N + BQ - 1) / BQ;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SOFTCAP>), dim3(unsigned(BHq) * unsigned(n_qblk)), dim3(kThreads),
+                     0, s, static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K),
+                     static_cast<const bf16_t*>(V), static_cast<const bf16_t*>(dO), LSE, Dv, dQacc, p.H, p.H_kv,
+                     p.N, BHq, p.scale, p.softcap);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t dq_d(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                const float* Dv, float* dQacc, hipStream_t s) {
+  const bool sc = p.softcap > 0.f;
+  if (p.causal) return sc ? dq_t<D, true, true>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
+                          : dq_t<D, true, false>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
+  return sc ? dq_t<D, false, true>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
+            : dq_t<D, false, false>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                              const float* LSE, const float* Dv, float* dQacc, hipStream_t s) {
+  return p.d == 64 ? dq_d<64>(p, Q, K, V, dO, LSE, Dv, dQacc, s) : dq_d<128>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
+}
+
+}  // namespace fabwd

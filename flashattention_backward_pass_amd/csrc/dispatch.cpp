@@ -12,8 +12,12 @@ hipError_t launch_fwd_stats(const Problem& p, const void* Q, const void* K, cons
 hipError_t launch_bwd(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                       const float* LSE, const float* D, float* dQacc, void* dK, void* dV, hipStream_t s) {
   (void)hipGetLastError();
-  // bf16: matrix-core kernel; fp32: vector-ALU kernel (same fp32 peak on MI355X).
-  if (p.dtype == 1) return launch_bwd_mfma(p, Q, K, V, dO, LSE, D, dQacc, dK, dV, s);
+  // bf16: matrix-core kernels; fp32: vector-ALU kernel (same fp32 peak on MI355X).
+  if (p.dtype == 1) {
+    hipError_t e = launch_bwd_dkdv_mfma(p, Q, K, V, dO, LSE, D, dK, dV, s);
+    if (e != hipSuccess) return e;
+    return launch_bwd_dq_mfma(p, Q, K, V, dO, LSE, D, dQacc, s);
+  }
   return launch_bwd_simple(p, Q, K, V, dO, LSE, D, dQacc, dK, dV, s);
 }
 

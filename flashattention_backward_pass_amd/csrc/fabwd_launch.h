@@ -32,7 +32,11 @@ hipError_t launch_fwd_simple(const Problem& p, const void* Q, const void* K, con
                              hipStream_t s);
 hipError_t launch_bwd_simple(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                              const float* LSE, const float* D, float* dQacc, void* dK, void* dV, hipStream_t s);
-hipError_t launch_bwd_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
-                           const float* LSE, const float* D, float* dQacc, void* dK, void* dV, hipStream_t s);
+// bf16 matrix-core backward: dK/dV kernel (key blocks outer) and dQ kernel
+// (query blocks outer); the dQ kernel overwrites dQaccum.
+hipError_t launch_bwd_dkdv_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                                const float* LSE, const float* D, void* dK, void* dV, hipStream_t s);
+hipError_t launch_bwd_dq_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                              const float* LSE, const float* D, float* dQacc, hipStream_t s);
 
 }  // namespace fabwd

@@ -1,5 +1,6 @@
 // Bandwidth-bound kernels of the backward pass:
-//   bwd_preprocess : D_i = sum_k dO_ik O_ik in fp32 and dQaccum <- 0
+//   bwd_preprocess : D_i = sum_k dO_ik O_ik in fp32, and dQaccum <- 0 for the
+//                    fp32 path (whose backward adds into dQaccum)
 //                    ("解析 FlashAttention（3）：FlashAttention-v1 反向传播", eq (6);
 //                     Inference Cookbook "反向传播算法详解" section 2.1, dPsum
 //                     computed before the backward kernel);
@@ -37,7 +38,7 @@ __device__ __forceinline__ void load16<bf16_t>(const bf16_t* p, float* out) {
 }
 
 // One lane handles 16 bytes of a row of O and dO.  Grid-stride over row groups.
-template <typename T, int D>
+template <typename T, int D, bool ZERO_ACC>
 __global__ __launch_bounds__(kThreads) void preprocess_kernel(const T* __restrict__ O, const T* __restrict__ dO,
                                                               float* __restrict__ Dout,
                                                               float* __restrict__ dQacc, int64_t rows) {
@@ -59,9 +60,11 @@ __global__ __launch_bounds__(kThreads) void preprocess_kernel(const T* __restric
       load16<T>(dO + off, g);
 #pragma unroll
       for (int e = 0; e < kPerLane; ++e) acc = fmaf(o[e], g[e], acc);
-      f32x4_t* z = reinterpret_cast<f32x4_t*>(dQacc + row * D) + lane_in_row * kZeroPerLane;
+      if (ZERO_ACC) {
+        f32x4_t* z = reinterpret_cast<f32x4_t*>(dQacc + row * D) + lane_in_row * kZeroPerLane;
 #pragma unroll
-      for (int e = 0; e < kZeroPerLane; ++e) z[e] = zero;
+        for (int e = 0; e < kZeroPerLane; ++e) z[e] = zero;
+      }
     }
     acc = wave_xor_sum(acc, L);
     if (row < rows && lane_in_row == 0) Dout[row] = acc;
@@ -118,7 +121,8 @@ template <typename T, int D>
 hipError_t preprocess_t(const Problem& p, const void* O, const void* dO, float* Dv, float* dQacc, hipStream_t s) {
   constexpr int L = D / (16 / sizeof(T));
   const int64_t rows = p.q_rows();
-  hipLaunchKernelGGL((preprocess_kernel<T, D>), dim3(grid_for(rows, kThreads / L)), dim3(kThreads), 0, s,
+  constexpr bool kZero = sizeof(T) == 4;  // only the fp32 backward accumulates into dQaccum
+  hipLaunchKernelGGL((preprocess_kernel<T, D, kZero>), dim3(grid_for(rows, kThreads / L)), dim3(kThreads), 0, s,
                      static_cast<const T*>(O), static_cast<const T*>(dO), Dv, dQacc, rows);
   return hipGetLastError();
 }

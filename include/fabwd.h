@@ -61,7 +61,7 @@ typedef struct attn_params {
   int32_t causal;           /* 0 or 1 */
   float scale;              /* softmax scale tau, finite and > 0 (usually 1/sqrt(d)) */
   float softcap;            /* c > 0 enables the tanh cap, 0 disables it */
-  int32_t deterministic;    /* must be 0: dQ partials are added with fp32 atomics */
+  int32_t deterministic;    /* reserved, must be 0 */
 } attn_params;
 
 /* Supported head dimensions: d = 64 and d = 128, for both dtypes. */
@@ -77,8 +77,10 @@ int attn_fwd_stats(const attn_params* p, const void* Q, const void* K, const voi
 
 /*
  * attn_bwd_preprocess - D = rowsum(dO o O) ([FA1] eq (6); [CB] 2.1 dPsum),
- * accumulated in float32, and dQaccum <- 0.
- * Reads O, dO; writes D [B,H,N] and zeroes dQaccum [B,H,N,d].
+ * accumulated in float32 in a fixed order (bitwise reproducible).
+ * Reads O, dO; writes D [B,H,N].  For fp32 inputs it also zeroes dQaccum
+ * [B,H,N,d] (the fp32 backward adds into it); for bf16 inputs dQaccum is not
+ * touched (the bf16 backward overwrites it).
  */
 int attn_bwd_preprocess(const attn_params* p, const void* O, const void* dO,
                         float* D, float* dQaccum, void* stream);
@@ -91,13 +93,18 @@ int attn_bwd_preprocess(const attn_params* p, const void* O, const void* dO,
  *   dP  = dO V^T                      ([FA1] eq (11))
  *   dS  = P o (dP - D), times (1 - tanh^2(R/c)) with a cap   ([FA1] eq (14); [CB] 2.1)
  *   dK += dS^T Q, scaled by `scale` once at the end            ([FA1] eq (16); [CB] 2.1)
- *   dQaccum += dS K (unscaled; fp32 atomics, [CB] 6.2)         ([FA1] eq (15))
+ *   dQaccum += dS K (unscaled)                                 ([FA1] eq (15))
  * Inputs: Q, K, V, dO (dtype), LSE from attn_fwd_stats, D from
- * attn_bwd_preprocess.  dQaccum must have been zeroed by attn_bwd_preprocess
- * on the same stream.  dK and dV are overwritten (not accumulated into).
- * dQaccum receives sum_j dS_ij K_j without the scale; attn_bwd_dq_convert
- * applies it.  The order of the fp32 additions into dQaccum is not fixed, so
- * its low bits may differ between runs.
+ * attn_bwd_preprocess on the same stream.  dK and dV are overwritten (not
+ * accumulated into).  dQaccum receives sum_j dS_ij K_j without the scale;
+ * attn_bwd_dq_convert applies it.
+ *   bf16: dK/dV come from a key-block-outer kernel and dQaccum from a
+ *         query-block-outer kernel that recomputes S and dP and keeps dQ in
+ *         registers; every row of dQaccum is overwritten with plain stores,
+ *         so the result is bitwise reproducible (no atomics).
+ *   fp32: one kernel adds the dQ partials of each key block into the zeroed
+ *         dQaccum with fp32 atomics; the order of those additions is not
+ *         fixed, so the low bits of dQ may differ between runs.
  */
 int attn_bwd(const attn_params* p, const void* Q, const void* K, const void* V,
              const void* dO, const float* LSE, const float* D,
