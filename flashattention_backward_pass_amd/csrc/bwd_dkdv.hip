@@ -10,8 +10,8 @@
 //   dP = dO_i V_j^T                     (GEMM 2)
 //   P  = exp2(S' tau log2e - LSE log2e), S' = c tanh(S/c) with a cap
 //   dS = P o (dP - D) [o (1 - tanh^2)]  rounded to bf16, P rounded to bf16
-//   dV += P^T dO_i                      (GEMM 3, [FA1] eq (10))
-//   dK += dS^T Q_i                      (GEMM 4, [FA1] eq (16))
+//   dV += P^T dO_i                      (GEMM 3, FlashAttention-v1 page eq (10))
+//   dK += dS^T Q_i                      (GEMM 4, FlashAttention-v1 page eq (16))
 // dK is multiplied by tau once in the epilogue (Cookbook 2.1).  dQ is
 // produced by the query-block-outer kernel in bwd_dq.hip.
 //
