@@ -24,11 +24,20 @@
 //    LDS tile with the transposing read ds_read_b64_tr_b16.
 //  * GEMM 1-4 run in two halves of 32 queries, so that only one 32x32 S and
 //    dP accumulator pair is live at a time.
+//  * K_j, V_j and the dK, dV accumulators are pinned to AGPRs (empty asm
+//    statements with an AGPR constraint): only matrix instructions touch them,
+//    and the VGPRs stay free for the softmax-gradient work without spills.
 //
-// Pipeline (one barrier per inner iteration):
+// Pipeline (one barrier per tile of 64 query rows):
 //   wait for tile t in LDS buffer t%2; barrier
-//   copy tile t+1 (Q, dO, LSE, D) global -> LDS buffer (t+1)%2 (global_load_lds)
+//   copy tile t+1 (Q, dO, LSE, D) global -> LDS buffer (t+1)%2 with buffer
+//   loads that write LDS directly (scalar tile offsets, no address VALU work)
 //   GEMM 1/2, softmax gradient, GEMM 3/4 of tile t
+//   wave 0 rescales the LSE of tile t+1 by log2(e) in LDS once it has landed
+// The loop is unrolled over the two buffers so every LDS offset is a
+// compile-time immediate.
+#include <type_traits>
+
 #include "fabwd_launch.h"
 #include "mfma_common.h"
 
@@ -54,7 +63,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(256))) float sD[2][BR];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;  // accumulator column / row group
   const int j16 = lane & 15, h16 = (lane >> 4) & 1;
 
@@ -78,6 +87,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     for (int c = 0; c < KC; ++c) {
       kreg[c] = load_bf16x8(K + row + 16 * c + 8 * g);
       vreg[c] = load_bf16x8(V + row + 16 * c + 8 * g);
+      // Only matrix instructions read K_j and V_j: keep them in AGPRs.
+      asm volatile("" : "+a"(kreg[c]));
+      asm volatile("" : "+a"(vreg[c]));
     }
   }
 
@@ -86,6 +98,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   for (int n = 0; n < NT; ++n) {
     dk_acc[n] = f32x16_t{};
     dv_acc[n] = f32x16_t{};
+    // dK, dV accumulate in AGPRs, leaving the VGPRs to the softmax-gradient work.
+    asm volatile("" : "+a"(dk_acc[n]));
+    asm volatile("" : "+a"(dv_acc[n]));
   }
 
   const float zs = scale * kLog2e;
@@ -101,14 +116,54 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   auto tile_q0 = [&](int t) { return (n_qblk - 1 - t % per_head) * BR; };
   auto tile_qoff = [&](int t) { return (int64_t(b) * H + hk * G + t / per_head) * N; };
 
-  auto issue_tile = [&](int t) {
-    const int buf = t & 1;
+  // Per-lane byte offsets of the tile copy: slab I = s*4 + w covers rows
+  // I*RPS .. I*RPS + RPS - 1; lane L fills physical chunk L % (D/8) of row
+  // I*RPS + L / (D/8), i.e. logical chunk (L % (D/8)) ^ swz(row).
+  constexpr int RPS = 1024 / (2 * D);          // rows per 1 KB slab
+  constexpr int NSLAB = BR / RPS / 4;          // slabs per wave
+  int dma_row[NSLAB], dma_col[NSLAB];
+#pragma unroll
+  for (int s = 0; s < NSLAB; ++s) {
+    const int row = (s * 4 + w) * RPS + lane / (D / 8);
+    dma_row[s] = row;
+    dma_col[s] = 8 * ((lane % (D / 8)) ^ swz<D>(row));
+  }
+
+  auto issue_tile = [&](auto bufc, int t) {
+    constexpr int buf = decltype(bufc)::value;
     const int q0 = tile_q0(t);
     const int64_t qoff = tile_qoff(t);
-    dma_tile<D, BR>(Q + (qoff + q0) * D, N - q0, sQ[buf], lane, w);
-    dma_tile<D, BR>(dO + (qoff + q0) * D, N - q0, sdO[buf], lane, w);
-    if (w == 0) dma4(LSE + qoff + min(q0 + lane, N - 1), &sL[buf][0]);
-    if (w == 1) dma4(Dv + qoff + min(q0 + lane, N - 1), &sD[buf][0]);
+    const int rows = min(BR, N - q0);
+    // Buffer resources over this tile's rows only; a ragged tile clamps its
+    // rows to the last valid one so every read stays inside the tensor.
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Q + (qoff + q0) * D), 0, rows * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ro =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(dO + (qoff + q0) * D), 0, rows * D * 2, 0x00020000);
+#pragma unroll
+    for (int s = 0; s < NSLAB; ++s) {
+      const int row = rows == BR ? dma_row[s] : min(dma_row[s], rows - 1);
+      const int voff = (row * D + dma_col[s]) * 2;
+      lds_void_t* dq = (lds_void_t*)&sQ[buf][(s * 4 + w) * 512];
+      lds_void_t* dd = (lds_void_t*)&sdO[buf][(s * 4 + w) * 512];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, dq, 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, dd, 16, voff, 0, 0, 0);
+    }
+    if (w < 2) {
+      const float* src = (w == 0 ? LSE : Dv) + qoff + q0;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, rows * 4, 0x00020000);
+      lds_void_t* dst = (lds_void_t*)(w == 0 ? &sL[buf][0] : &sD[buf][0]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, min(lane, rows - 1) * 4, 0, 0, 0);
+    }
+  };
+  // Wave 0: once the LSE of buffer BUF has landed, turn it into LSE * log2(e)
+  // in place (published to the other waves by the next barrier).
+  auto prescale_lse = [&](auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    if (w == 0) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      sL[buf][lane] *= kLog2e;
+    }
   };
 
   // Softmax gradient of 32 queries (rows qbase..qbase+31 of the tile):
@@ -129,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
           s = softcap * th;
           dt = 1.f - th * th;
         }
-        float p = fast_exp2(fmaf(s, zs, -l4[e] * kLog2e));
+        float p = fast_exp2(fmaf(s, zs, -l4[e]));
         if (masked) {
           const int qg = q0 + qr + e;
           if (my_key >= N || qg >= N || (CAUSAL && my_key > qg)) p = 0.f;
@@ -142,14 +197,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     }
   };
 
-  issue_tile(0);
-  for (int t = 0; t < n_iter; ++t) {
-    const int buf = t & 1;
+  auto do_tile = [&](auto bufc, int t) {
+    constexpr int buf = decltype(bufc)::value;
     const int q0 = tile_q0(t);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile t in LDS; buffer (t+1)%2 no longer read
-    if (t + 1 < n_iter) issue_tile(t + 1);
-
     const bool masked = (CAUSAL && q0 < k0 + BC) || ragged_keys || q0 + BR > N;
 #pragma unroll
     for (int tq = 0; tq < 2; ++tq) {
@@ -191,7 +241,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
           dv_acc[n] = mfma32(pf[u], ob, dv_acc[n]);
           dk_acc[n] = mfma32(dsf[u], qb, dk_acc[n]);
         }
+        asm volatile("" : "+a"(dv_acc[n]));
+        asm volatile("" : "+a"(dk_acc[n]));
       }
+    }
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  issue_tile(B0{}, 0);
+  prescale_lse(B0{});
+  for (int t = 0; t < n_iter; t += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile t in buffer 0; buffer 1 no longer read
+    if (t + 1 < n_iter) issue_tile(B1{}, t + 1);
+    do_tile(B0{}, t);
+    if (t + 1 < n_iter) {
+      prescale_lse(B1{});
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // tile t+1 in buffer 1; buffer 0 no longer read
+      if (t + 2 < n_iter) issue_tile(B0{}, t + 2);
+      do_tile(B1{}, t + 1);
+      if (t + 2 < n_iter) prescale_lse(B0{});
     }
   }
 

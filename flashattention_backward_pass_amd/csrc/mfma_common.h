@@ -44,13 +44,20 @@ __device__ __forceinline__ bf16x8_t pack_bf16x8(const f32x16_t& v, int base) {
 }
 
 // Bf16 tiles of D columns live in LDS with unpadded rows whose 16-byte chunks
-// are XOR-swizzled by row.  Over 16 consecutive rows the swizzle is a
-// permutation (16-byte row reads by 16 lanes hit 16 distinct bank groups) and
-// over 4 aligned consecutive rows it maps a 32-byte chunk pair to 4 distinct
-// pairs (the transposing reads of 4 rows x 32 bytes hit distinct banks).
+// are XOR-swizzled by row.  Two access patterns must stay free of bank
+// conflicts (64 banks of 4 bytes; a 16-byte read is served 16 lanes at a time,
+// an 8-byte read 32 lanes at a time):
+//  * row reads: 16 lanes read the same logical chunk of 16 consecutive rows,
+//    so over 16 aligned rows the swizzle must be a permutation;
+//  * transposing reads: 32 lanes read an aligned group of 4 chunks (64 bytes)
+//    in each of 4 aligned consecutive rows, so those 4 rows must move the
+//    group to 4 different positions.
+// d = 128 (16 chunks per 256-byte row): swz = 4 (r % 4) + (r / 4) % 4.
+// d = 64 (8 chunks per 128-byte row, two rows per bank window):
+// swz = 4 ((r / 2) % 2) + (r / 4) % 4.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if (D == 128) return ((row & 3) << 1) | ((row >> 2) & 1) | (((row >> 3) & 1) << 3);
+  if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
   return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
