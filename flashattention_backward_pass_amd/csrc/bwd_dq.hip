@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __attribute__((aligned(1024))) uint16_t sV[2][BK * D];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int j16 = lane & 15, h16 = (lane >> 4) & 1;
 
@@ -79,10 +79,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int kv_end = CAUSAL ? min(N, q0 + BQ) : N;
   const int n_steps = (kv_end + BK - 1) / BK;
 
+  // Per-lane byte offsets of the K/V block copies: slab I = s*4 + w covers
+  // rows I*RPS ..; lane L fills physical chunk L % (D/8) of row I*RPS + L/(D/8),
+  // i.e. logical chunk (L % (D/8)) ^ swz(row).
+  constexpr int RPS = 1024 / (2 * D);
+  constexpr int NSLAB = BK / RPS / 4;
+  int dma_voff[NSLAB];
+#pragma unroll
+  for (int s = 0; s < NSLAB; ++s) {
+    const int row = (s * 4 + w) * RPS + lane / (D / 8);
+    dma_voff[s] = (row * D + 8 * ((lane % (D / 8)) ^ swz<D>(row))) * 2;
+  }
+  // Copy key/value block `step` into LDS buffer step%2 with buffer loads that
+  // write LDS directly (scalar base per block; a ragged block clamps its rows
+  // to the last valid key).
   auto issue = [&](int step) {
     const int kb = step * BK;
-    dma_tile<D, BK>(K + (kv_off + kb) * D, N - kb, sK[step & 1], lane, w);
-    dma_tile<D, BK>(V + (kv_off + kb) * D, N - kb, sV[step & 1], lane, w);
+    const int rows = min(BK, N - kb);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(K + (kv_off + kb) * D), 0, rows * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(V + (kv_off + kb) * D), 0, rows * D * 2, 0x00020000);
+#pragma unroll
+    for (int s = 0; s < NSLAB; ++s) {
+      int voff = dma_voff[s];
+      if (rows < BK) {
+        const int row = min((s * 4 + w) * RPS + lane / (D / 8), rows - 1);
+        voff = (row * D + 8 * ((lane % (D / 8)) ^ swz<D>((s * 4 + w) * RPS + lane / (D / 8)))) * 2;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)&sK[step & 1][(s * 4 + w) * 512], 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&sV[step & 1][(s * 4 + w) * 512], 16, voff, 0, 0, 0);
+    }
   };
 
   issue(0);
