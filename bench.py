@@ -81,8 +81,9 @@ def copy_calibration(torch):
                       "GBs": 2 * n * 4 / dt / 1e9}), flush=True)
 
 
-def cpu_baseline(w, x):
-    """The fp64 oracle, untuned, on one query head of the workload at full N."""
+def cpu_baseline(w, x, heads=3):
+    """The fp64 oracle, untuned, on the first `heads` query heads of batch 0 of
+    the workload at full N (about 4 s of host time per head at N = 16384)."""
     import numpy as np
     import oracle
     try:
@@ -90,15 +91,19 @@ def cpu_baseline(w, x):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
-    q, k, v, do = (x[n][0, 0] for n in ("Q", "K", "V", "dO"))
+    heads = min(heads, w.H)
+    group = w.H // w.H_kv
     t0 = time.perf_counter()
-    O, L = oracle.forward_head(q, k, v, w.tau, w.causal, w.softcap)
-    oracle.backward_head(q, k, v, O, do, L, w.tau, w.causal, w.softcap)
+    for h in range(heads):
+        q, do = x["Q"][0, h], x["dO"][0, h]
+        k, v = x["K"][0, h // group], x["V"][0, h // group]
+        O, L = oracle.forward_head(q, k, v, w.tau, w.causal, w.softcap)
+        oracle.backward_head(q, k, v, O, do, L, w.tau, w.causal, w.softcap)
     dt = time.perf_counter() - t0
-    flops = 10.0 * w.N * w.N * w.d / (2.0 if w.causal else 1.0)
+    flops = heads * 10.0 * w.N * w.N * w.d / (2.0 if w.causal else 1.0)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"one query head (b=0, h=0) of the workload at full N={w.N}: fp64 forward + backward, "
-                      f"{dt:.1f} s wall; metric FLOPs of that head",
+            "sample": f"{heads} query heads (b=0, h=0..{heads - 1}) of the workload at full N={w.N}: "
+                      f"fp64 forward + backward, {dt:.1f} s wall; metric FLOPs of those heads",
             "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
 
 
