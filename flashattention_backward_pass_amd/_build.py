@@ -42,13 +42,21 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-file flags.  bwd_dkdv.hip keeps every matrix accumulator in VGPRs
+# (the softmax-gradient VALU work reads S and dP straight from them; the
+# K/V operand slices are pinned to AGPRs in the source).
+FILE_FLAGS = {
+    "bwd_dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
@@ -76,8 +84,23 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link of libfabwd.so failed:\n{r.stdout}{r.stderr}")
+    _check_kernel_stubs(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_kernel_stubs(lib: str) -> None:
+    """Fails if a kernel launch stub is missing from the library: the host
+    compilation can drop a kernel without a diagnostic (seen with array
+    elements passed straight into buffer-load builtins), which would only
+    surface as an unresolved symbol when the library is loaded."""
+    nm = shutil.which("nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    r = subprocess.run([nm, "-D", "--undefined-only", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"nm failed on {lib}:\n{r.stderr}")
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError("kernel launch stubs missing from libfabwd.so: " + ", ".join(missing))
 
 
 if __name__ == "__main__":

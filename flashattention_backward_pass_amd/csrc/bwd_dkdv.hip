@@ -22,18 +22,21 @@
 //    those GEMMs (queries) follows the accumulator's row order; the matching
 //    B operand (dO_i, Q_i with queries along k) is read from the row-major
 //    LDS tile with the transposing read ds_read_b64_tr_b16.
-//  * GEMM 1-4 run in two halves of 32 queries, so that only one 32x32 S and
-//    dP accumulator pair is live at a time.
-//  * K_j, V_j and the dK, dV accumulators are pinned to AGPRs (empty asm
-//    statements with an AGPR constraint): only matrix instructions touch them,
-//    and the VGPRs stay free for the softmax-gradient work without spills.
+//  * The S and dP accumulators start from values read out of LDS instead of
+//    zero.  S starts at -LSE/tau, so P = exp2(tau log2e * S_acc).  The V
+//    slice is held negated and dP starts at +D, so the dP accumulator ends at
+//    D - dP and P * acc = -dS; the sign is folded into dK's epilogue scale.
+//    Masked positions start S at -inf.  The softmax gradient is one
+//    multiply, one exp2 and one multiply per element.
+//  * All matrix instructions use VGPR accumulators (the file is built with
+//    -mllvm -amdgpu-mfma-vgpr-form); the K_j, V_j slices, only ever read as
+//    matrix operands, are pinned to AGPRs.
 //
-// Pipeline (one barrier per tile of 64 query rows):
-//   wait for tile t in LDS buffer t%2; barrier
-//   copy tile t+1 (Q, dO, LSE, D) global -> LDS buffer (t+1)%2 with buffer
-//   loads that write LDS directly (scalar tile offsets, no address VALU work)
-//   GEMM 1/2, softmax gradient, GEMM 3/4 of tile t
-//   wave 0 rescales the LSE of tile t+1 by log2(e) in LDS once it has landed
+// Pipeline (one barrier per tile of 64 query rows, two LDS buffers):
+//   tile t: A(0) | A(1) + B(0) | C(0) + B(1) | C(1)   (see do_tile)
+//   the copies of tile t+1 (Q, dO, LSE, D; buffer loads that write LDS
+//   directly) are issued between the matrix instructions of A(0); wave 0
+//   rescales the LSE of tile t+1 in LDS during C(1); then wait + barrier.
 // The loop is unrolled over the two buffers so every LDS offset is a
 // compile-time immediate.
 #include <type_traits>
@@ -49,6 +52,12 @@ constexpr int kThreads = 256;
 constexpr int BC = 128;  // keys per workgroup
 constexpr int BR = 64;   // query rows per inner iteration
 
+// Position in the sequence of query tiles of a workgroup.
+struct Cursor {
+  int q0;        // first row of the query block
+  int64_t row0;  // (b*H + h)*N, row offset of the query head
+};
+
 template <int D, bool CAUSAL, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
@@ -57,10 +66,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     float softcap) {
   constexpr int KC = D / 16;  // 16-wide k chunks over d
   constexpr int NT = D / 32;  // 32-wide column tiles over d
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ[2][BR * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sdO[2][BR * D];
-  __shared__ __attribute__((aligned(256))) float sL[2][BR];
-  __shared__ __attribute__((aligned(256))) float sD[2][BR];
+  // Double buffers as separate variables: the compiler gives each LDS
+  // variable its own alias scope, so reads of one buffer do not wait for the
+  // asynchronous copies still landing in the other.
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ0[BR * D], sQ1[BR * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sdO0[BR * D], sdO1[BR * D];
+  __shared__ __attribute__((aligned(256))) float sL0[BR], sL1[BR];
+  __shared__ __attribute__((aligned(256))) float sD0[BR], sD1[BR];
+  __shared__ float sX[4][BR];  // rows rescaled by waves 1-3 in place of the LSE
+  auto bufsel = [](auto bufc, auto* a0, auto* a1) {
+    if constexpr (decltype(bufc)::value == 0) return a0;
+    else return a1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -78,7 +95,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int kw = w * 32;                                 // this wave's first key in the block
   const int my_key = k0 + kw + l32;                      // key owned by this lane in GEMM 1/2
 
-  // K_j, V_j slices: B operands of GEMM 1/2, resident for the whole loop.
+  // K_j and -V_j slices: B operands of GEMM 1/2, resident for the whole loop.
   // Keys past N read row N-1: their P is masked to 0, so they contribute nothing.
   bf16x8_t kreg[KC], vreg[KC];
   {
@@ -86,8 +103,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       kreg[c] = load_bf16x8(K + row + 16 * c + 8 * g);
-      vreg[c] = load_bf16x8(V + row + 16 * c + 8 * g);
-      // Only matrix instructions read K_j and V_j: keep them in AGPRs.
+      const u32x4_t vb = *reinterpret_cast<const u32x4_t*>(V + row + 16 * c + 8 * g);
+      vreg[c] = __builtin_bit_cast(bf16x8_t, vb ^ 0x80008000u);
+      // Only matrix instructions read them: keep them in AGPRs.
       asm volatile("" : "+a"(kreg[c]));
       asm volatile("" : "+a"(vreg[c]));
     }
@@ -98,175 +116,314 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   for (int n = 0; n < NT; ++n) {
     dk_acc[n] = f32x16_t{};
     dv_acc[n] = f32x16_t{};
-    // dK, dV accumulate in AGPRs, leaving the VGPRs to the softmax-gradient work.
-    asm volatile("" : "+a"(dk_acc[n]));
-    asm volatile("" : "+a"(dv_acc[n]));
   }
 
   const float zs = scale * kLog2e;
+  const float lse_mul = SOFTCAP ? kLog2e : -1.f / scale;
   const int n_qblk = (N + BR - 1) / BR;
   const int i_first = CAUSAL ? (k0 / BR) : 0;
-  const int per_head = n_qblk - i_first;
-  const int n_iter = per_head * G;
+  const int n_iter = (n_qblk - i_first) * G;
   const bool ragged_keys = k0 + BC > N;
+  const int q_last = (n_qblk - 1) * BR;  // first row of the last (possibly ragged) query block
+  const int rows_last = N - q_last;      // its valid rows
 
-  // Tile t of the flattened (query head, query block) sequence; query blocks
-  // run from the last one down, so concurrent workgroups of a head sweep the
-  // same rows together.
-  auto tile_q0 = [&](int t) { return (n_qblk - 1 - t % per_head) * BR; };
-  auto tile_qoff = [&](int t) { return (int64_t(b) * H + hk * G + t / per_head) * N; };
+  // Tiles run over the query heads of the group and, within a head, over the
+  // query blocks from the last one down (concurrent workgroups of a head sweep
+  // the same rows together).  A cursor steps through that sequence without
+  // divisions; one cursor feeds the copies, one the compute.
+  const int64_t head0 = (int64_t(b) * H + hk * G) * N;
+  auto advance = [&](Cursor& c) {
+    if (c.q0 == i_first * BR) {
+      c.q0 = q_last;
+      c.row0 += N;
+    } else {
+      c.q0 -= BR;
+    }
+  };
 
   // Per-lane byte offsets of the tile copy: slab I = s*4 + w covers rows
   // I*RPS .. I*RPS + RPS - 1; lane L fills physical chunk L % (D/8) of row
-  // I*RPS + L / (D/8), i.e. logical chunk (L % (D/8)) ^ swz(row).
-  constexpr int RPS = 1024 / (2 * D);          // rows per 1 KB slab
-  constexpr int NSLAB = BR / RPS / 4;          // slabs per wave
-  int dma_row[NSLAB], dma_col[NSLAB];
+  // I*RPS + L / (D/8), i.e. logical chunk (L % (D/8)) ^ swz(row).  Each copy's
+  // buffer descriptor spans only the tile's valid rows: reads past N return
+  // zeros (rows that are masked anyway), and the LDS tiles start zeroed.
+  constexpr int RPS = 1024 / (2 * D);  // rows per 1 KB slab
+  constexpr int NSLAB = BR / RPS / 4;  // slabs per wave and tensor
+  constexpr int NDMA = 2 * NSLAB + 1;  // copies per wave and tile (Q, dO, LSE or D)
+  int voff[NSLAB];
 #pragma unroll
   for (int s = 0; s < NSLAB; ++s) {
     const int row = (s * 4 + w) * RPS + lane / (D / 8);
-    dma_row[s] = row;
-    dma_col[s] = 8 * ((lane % (D / 8)) ^ swz<D>(row));
+    voff[s] = (row * D + 8 * ((lane % (D / 8)) ^ swz<D>(row))) * 2;
   }
 
-  auto issue_tile = [&](auto bufc, int t) {
-    constexpr int buf = decltype(bufc)::value;
-    const int q0 = tile_q0(t);
-    const int64_t qoff = tile_qoff(t);
-    const int rows = min(BR, N - q0);
-    // Buffer resources over this tile's rows only; a ragged tile clamps its
-    // rows to the last valid one so every read stays inside the tensor.
-    const __amdgpu_buffer_rsrc_t rq =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Q + (qoff + q0) * D), 0, rows * D * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t ro =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(dO + (qoff + q0) * D), 0, rows * D * 2, 0x00020000);
-#pragma unroll
-    for (int s = 0; s < NSLAB; ++s) {
-      const int row = rows == BR ? dma_row[s] : min(dma_row[s], rows - 1);
-      const int voff = (row * D + dma_col[s]) * 2;
-      lds_void_t* dq = (lds_void_t*)&sQ[buf][(s * 4 + w) * 512];
-      lds_void_t* dd = (lds_void_t*)&sdO[buf][(s * 4 + w) * 512];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, dq, 16, voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, dd, 16, voff, 0, 0, 0);
-    }
-    if (w < 2) {
-      const float* src = (w == 0 ? LSE : Dv) + qoff + q0;
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, rows * 4, 0x00020000);
-      lds_void_t* dst = (lds_void_t*)(w == 0 ? &sL[buf][0] : &sD[buf][0]);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, min(lane, rows - 1) * 4, 0, 0, 0);
+  // Copy k (0 .. NDMA-1) of the tile at cursor c into buffer BUF.  Each
+  // buffer descriptor spans the tile's valid rows of Q, dO, and LSE (wave 0)
+  // or D (wave 1).  (The buffer builtins get plain local values: an array
+  // element written directly as an argument makes the host compilation
+  // silently drop the kernel.)
+  auto copy_one = [&](auto bufc, const Cursor& c, int k) {
+    const int rows = min(BR, N - c.q0);
+    const int64_t r0 = c.row0 + c.q0;
+    if (k < 2 * NSLAB) {
+      const int s = k % NSLAB;
+      const int vo = voff[s];
+      const bf16_t* src = k < NSLAB ? Q : dO;
+      uint16_t* dst = k < NSLAB ? bufsel(bufc, sQ0, sQ1) : bufsel(bufc, sdO0, sdO1);
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)(src + r0 * D), 0, rows * D * 2, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)&dst[(s * 4 + w) * 512], 16, vo, 0, 0, 0);
+    } else if (w < 2) {
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc((void*)((w == 0 ? LSE : Dv) + r0), 0, rows * 4, 0x00020000);
+      float* dst = w == 0 ? bufsel(bufc, sL0, sL1) : bufsel(bufc, sD0, sD1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 4, lane * 4, 0, 0, 0);
     }
   };
-  // Wave 0: once the LSE of buffer BUF has landed, turn it into LSE * log2(e)
-  // in place (published to the other waves by the next barrier).
-  auto prescale_lse = [&](auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    if (w == 0) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      sL[buf][lane] *= kLog2e;
-    }
+  // Once its copy of the LSE into buffer BUF has landed, wave 0 turns it into
+  // -LSE/tau in place (LSE log2e with a soft cap), published by the next
+  // barrier.  Waves 1-3 run the same instructions on a row of their own, so
+  // there is no branch.
+  auto prescale = [&](auto bufc) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    float* l = w == 0 ? bufsel(bufc, sL0, sL1) : &sX[w][0];
+    l[lane] *= lse_mul;
   };
 
-  // Softmax gradient of 32 queries (rows qbase..qbase+31 of the tile):
-  // s_acc <- P, dp_acc <- dS (both fp32).
-  auto softmax_grad = [&](f32x16_t& s_acc, f32x16_t& dp_acc, int buf, int q0, int qbase, bool masked) {
+  // Per-lane LDS offsets (elements), fixed for the whole loop; the half,
+  // the buffer and the 16-row step add compile-time constants.
+  //  * row reads (A operand of S, dP): row l32, logical chunk 2c + g;
+  //  * transposing reads (B operand of dV, dK): row 4g + j16/4 (+8), logical
+  //    chunk 4n + 2 h16 + (j16 % 4)/2, element 4 (j16 % 2) within the chunk.
+  // The swizzle only depends on the row modulo 16, so rows +16 and +32 share it.
+  int off_a[KC], off_t[NT][2];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int qr = qbase + 8 * m + 4 * g;
-      const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&sL[buf][qr]);
-      const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&sD[buf][qr]);
+  for (int c = 0; c < KC; ++c) off_a[c] = swz_off<D>(l32, 2 * c + g, 0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * m + e;
-        float s = s_acc[r];
-        float dt = 1.f;
-        if (SOFTCAP) {
-          const float th = tanh_f32(s / softcap);
-          s = softcap * th;
-          dt = 1.f - th * th;
-        }
-        float p = fast_exp2(fmaf(s, zs, -l4[e]));
-        if (masked) {
-          const int qg = q0 + qr + e;
-          if (my_key >= N || qg >= N || (CAUSAL && my_key > qg)) p = 0.f;
-        }
-        s_acc[r] = p;
-        float ds = p * (dp_acc[r] - d4[e]);
-        if (SOFTCAP) ds *= dt;
-        dp_acc[r] = ds;
-      }
-    }
-  };
+  for (int n = 0; n < NT; ++n) {
+    const int ch = 4 * n + 2 * h16 + ((j16 & 3) >> 1);
+#pragma unroll
+    for (int v = 0; v < 2; ++v) off_t[n][v] = swz_off<D>(4 * g + (j16 >> 2) + 8 * v, ch, 4 * (j16 & 1));
+  }
 
-  auto do_tile = [&](auto bufc, int t) {
-    constexpr int buf = decltype(bufc)::value;
-    const int q0 = tile_q0(t);
-    const bool masked = (CAUSAL && q0 < k0 + BC) || ragged_keys || q0 + BR > N;
+  // One tile of 64 query rows in two halves h = 0, 1 of 32 rows:
+  //   A(h): S_h, dP_h accumulate over d (2 MFMAs per 16-wide chunk of d)
+  //   B(h): P and dS of half h, packed to bf16 (VALU)
+  //   C(h): dV += P_h^T dO_h, dK += dS_h^T Q_h (2 MFMAs per (u, n) step)
+  // issued as A(0) | A(1) + B(0) | C(0) + B(1) | C(1), so the softmax
+  // gradient of one half runs under the matrix instructions of the other.
+  // Each stage is a fixed sequence of slots (2 MFMAs, the LDS reads for a
+  // later slot, a share of the other work) separated by scheduling barriers,
+  // so the compiler keeps this order and its register use stays bounded.
+  // `next` is the tile whose copies go out during A(0), into the other buffer.
+  auto do_tile = [&](auto bufc, int q0, bool masked, const Cursor& next) {
+    using NB = std::integral_constant<int, 1 - decltype(bufc)::value>;
+    const uint16_t* tq_ = bufsel(bufc, sQ0, sQ1);
+    const uint16_t* to_ = bufsel(bufc, sdO0, sdO1);
+    const float* sl_ = bufsel(bufc, sL0, sL1);
+    const float* sd_ = bufsel(bufc, sD0, sD1);
+    auto rowop = [&](const uint16_t* t, int h, int c) {
+      return *reinterpret_cast<const bf16x8_t*>(&t[off_a[c] + 32 * h * D]);
+    };
+    auto trop = [&](const uint16_t* t, int h, int u, int n) {
+      return cat8(lds_read_tr(&t[off_t[n][0] + (32 * h + 16 * u) * D]),
+                  lds_read_tr(&t[off_t[n][1] + (32 * h + 16 * u) * D]));
+    };
+    auto acc_init = [&](const float* src, int h) {
+      f32x16_t a;
 #pragma unroll
-    for (int tq = 0; tq < 2; ++tq) {
-      // GEMM 1, 2: S and dP for queries 32 tq .. 32 tq + 31 x this wave's 32 keys.
-      f32x16_t s_acc = {}, dp_acc = {};
-      const int row = 32 * tq + l32;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const int off = swz_off<D>(row, 2 * c + g, 0);
-        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(&sQ[buf][off]);
-        const bf16x8_t oa = *reinterpret_cast<const bf16x8_t*>(&sdO[buf][off]);
-        s_acc = mfma32(qa, kreg[c], s_acc);
-        dp_acc = mfma32(oa, vreg[c], dp_acc);
+      for (int m = 0; m < 4; ++m) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&src[32 * h + 8 * m + 4 * g]);
+        a[4 * m] = v[0];
+        a[4 * m + 1] = v[1];
+        a[4 * m + 2] = v[2];
+        a[4 * m + 3] = v[3];
       }
-      // P and dS.  Accumulator register r holds query 32 tq + 8(r/4) + 4g + r%4, key my_key.
-      if (masked)
-        softmax_grad(s_acc, dp_acc, buf, q0, 32 * tq, true);
-      else
-        softmax_grad(s_acc, dp_acc, buf, q0, 32 * tq, false);
-      // bf16 A operands: chunk u (16 queries) = registers 8u..8u+7.
-      bf16x8_t pf[2], dsf[2];
+      return a;
+    };
+    // Masked tiles: positions outside the causal triangle or past N start S
+    // at -inf (so P = exp2(-inf) = 0 and dS = 0); with a soft cap the
+    // subtracted LSE becomes +inf instead.  Applied to the initial values only.
+    auto mask_init = [&](f32x16_t& a, int h) {
+      const float fill = SOFTCAP ? __builtin_inff() : -__builtin_inff();
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        pf[u] = pack_bf16x8(s_acc, 8 * u);
-        dsf[u] = pack_bf16x8(dp_acc, 8 * u);
+      for (int r = 0; r < 16; ++r) {
+        const int qg = q0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool ok = CAUSAL ? (qg >= my_key && qg < N) : (qg < N && my_key < N);
+        a[r] = ok ? a[r] : fill;
       }
-      // GEMM 3, 4: dV += P^T dO_i, dK += dS^T Q_i over these 32 queries.
-      // B operand rows (queries) 32 tq + 16u + 4g + (0..3) and +8, read transposed.
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const int ch = 4 * n + 2 * h16 + ((j16 & 3) >> 1);
-        const int sub = 4 * (j16 & 1);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r0 = 32 * tq + 16 * u + 4 * g + (j16 >> 2);
-          const int o0 = swz_off<D>(r0, ch, sub), o1 = swz_off<D>(r0 + 8, ch, sub);
-          const bf16x8_t ob = cat8(lds_read_tr(&sdO[buf][o0]), lds_read_tr(&sdO[buf][o1]));
-          const bf16x8_t qb = cat8(lds_read_tr(&sQ[buf][o0]), lds_read_tr(&sQ[buf][o1]));
-          dv_acc[n] = mfma32(pf[u], ob, dv_acc[n]);
-          dk_acc[n] = mfma32(dsf[u], qb, dk_acc[n]);
-        }
-        asm volatile("" : "+a"(dv_acc[n]));
-        asm volatile("" : "+a"(dk_acc[n]));
+    };
+    // The softmax gradient of one element in three steps, software-pipelined
+    // over the slots of a stage (slot i runs step 1 of its elements, step 2 of
+    // the previous slot's and step 3 of the one before), so consecutive VALU
+    // instructions are independent.
+    //   1: t = S_acc * tau log2e  (cap: t = c tanh(S/c) tau log2e - LSE log2e)
+    //   2: P = exp2(t)
+    //   3: -dS = P * dP_acc [* (1 - tanh^2)]; bf16 pairs packed
+    auto step1 = [&](f32x16_t& sa, f32x16_t& la, int r) {
+      if (SOFTCAP) {
+        const float th = tanh_f32(sa[r] / softcap);
+        sa[r] = fmaf(softcap * th, zs, -la[r]);
+        la[r] = 1.f - th * th;
+      } else {
+        sa[r] = sa[r] * zs;
       }
+    };
+    auto step2 = [&](f32x16_t& sa, int r) { sa[r] = fast_exp2(sa[r]); };
+    auto step3 = [&](f32x16_t& sa, f32x16_t& da, const f32x16_t& la, u32x4_t* pw, u32x4_t* dw, int r) {
+      float ds = sa[r] * da[r];
+      if (SOFTCAP) ds *= la[r];
+      da[r] = ds;
+      if (r & 1) {
+        pw[r >> 3][(r & 7) >> 1] = pack_bf16x2(sa[r - 1], sa[r]);
+        dw[r >> 3][(r & 7) >> 1] = pack_bf16x2(da[r - 1], ds);
+      }
+    };
+    // Pipeline position `slot` of a stage with E elements per slot; slots past
+    // the stage's own (16 / E) only drain steps 2 and 3.
+    auto sm_slot = [&](f32x16_t& sa, f32x16_t& da, f32x16_t& la, u32x4_t* pw, u32x4_t* dw, int E, int slot) {
+      const int ns = 16 / E;
+      if (slot < ns)
+        for (int e = 0; e < E; ++e) step1(sa, la, E * slot + e);
+      if (slot >= 1 && slot - 1 < ns)
+        for (int e = 0; e < E; ++e) step2(sa, E * (slot - 1) + e);
+      if (slot >= 2 && slot - 2 < ns)
+        for (int e = 0; e < E; ++e) step3(sa, da, la, pw, dw, E * (slot - 2) + e);
+    };
+
+    constexpr int PF = 2;              // row-operand prefetch distance (chunks)
+    constexpr int EA = 16 / KC;        // softmax elements per A slot
+    constexpr int EC = 16 / (2 * NT);  // softmax elements per C slot
+    f32x16_t s0, d0, s1, d1, l0 = {}, l1 = {};
+    u32x4_t pw0[2], dw0[2], pw1[2], dw1[2];
+    bf16x8_t qa[KC], oa[KC];
+
+    // ---- A(0), with the copies of the next tile ----
+    s0 = SOFTCAP ? f32x16_t{} : acc_init(sl_, 0);
+    if (SOFTCAP) l0 = acc_init(sl_, 0);
+    d0 = acc_init(sd_, 0);
+    if (masked) mask_init(SOFTCAP ? l0 : s0, 0);
+#pragma unroll
+    for (int c = 0; c < PF; ++c) {
+      qa[c] = rowop(tq_, 0, c);
+      oa[c] = rowop(to_, 0, c);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if (c + PF < KC) {
+        qa[c + PF] = rowop(tq_, 0, c + PF);
+        oa[c + PF] = rowop(to_, 0, c + PF);
+      } else {
+        // The first chunks of half 1.
+        const int c1 = c + PF - KC;
+        qa[c1] = rowop(tq_, 1, c1);
+        oa[c1] = rowop(to_, 1, c1);
+      }
+      s0 = mfma32(qa[c], kreg[c], s0);
+      d0 = mfma32(oa[c], vreg[c], d0);
+#pragma unroll
+      for (int k = c; k < NDMA; k += KC) copy_one(NB{}, next, k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s1 = SOFTCAP ? f32x16_t{} : acc_init(sl_, 1);
+    if (SOFTCAP) l1 = acc_init(sl_, 1);
+    d1 = acc_init(sd_, 1);
+    if (masked) mask_init(SOFTCAP ? l1 : s1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- A(1) + B(0) ----
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if (c + PF < KC) {
+        qa[c + PF] = rowop(tq_, 1, c + PF);
+        oa[c + PF] = rowop(to_, 1, c + PF);
+      }
+      s1 = mfma32(qa[c], kreg[c], s1);
+      d1 = mfma32(oa[c], vreg[c], d1);
+      sm_slot(s0, d0, l0, pw0, dw0, EA, c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- C(0) + B(1) ----  slot i: u = i / NT, n = i % NT
+    bf16x8_t ob[2], qb[2];
+    ob[0] = trop(to_, 0, 0, 0);
+    qb[0] = trop(tq_, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * NT; ++i) {
+      const int u = i / NT, n = i % NT;
+      if (i + 1 < 2 * NT) {
+        ob[(i + 1) & 1] = trop(to_, 0, (i + 1) / NT, (i + 1) % NT);
+        qb[(i + 1) & 1] = trop(tq_, 0, (i + 1) / NT, (i + 1) % NT);
+      } else {
+        ob[(i + 1) & 1] = trop(to_, 1, 0, 0);
+        qb[(i + 1) & 1] = trop(tq_, 1, 0, 0);
+      }
+      dv_acc[n] = mfma32(__builtin_bit_cast(bf16x8_t, pw0[u]), ob[i & 1], dv_acc[n]);
+      dk_acc[n] = mfma32(__builtin_bit_cast(bf16x8_t, dw0[u]), qb[i & 1], dk_acc[n]);
+      // Drain B(0) in the first two slots; B(1) runs alongside.
+      if (i < 2) sm_slot(s0, d0, l0, pw0, dw0, EA, KC + i);
+      sm_slot(s1, d1, l1, pw1, dw1, EC, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- C(1) ----  (2 NT is even: slot i reads buffer i & 1 again)
+#pragma unroll
+    for (int i = 0; i < 2 * NT; ++i) {
+      const int u = i / NT, n = i % NT;
+      if (i + 1 < 2 * NT) {
+        ob[(i + 1) & 1] = trop(to_, 1, (i + 1) / NT, (i + 1) % NT);
+        qb[(i + 1) & 1] = trop(tq_, 1, (i + 1) / NT, (i + 1) % NT);
+      }
+      dv_acc[n] = mfma32(__builtin_bit_cast(bf16x8_t, pw1[u]), ob[i & 1], dv_acc[n]);
+      dk_acc[n] = mfma32(__builtin_bit_cast(bf16x8_t, dw1[u]), qb[i & 1], dk_acc[n]);
+      if (i < 2) sm_slot(s1, d1, l1, pw1, dw1, EC, 2 * NT + i);
+      if (i == 2) prescale(NB{});
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  issue_tile(B0{}, 0);
-  prescale_lse(B0{});
-  for (int t = 0; t < n_iter; t += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile t in buffer 0; buffer 1 no longer read
-    if (t + 1 < n_iter) issue_tile(B1{}, t + 1);
-    do_tile(B0{}, t);
-    if (t + 1 < n_iter) {
-      prescale_lse(B1{});
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // tile t+1 in buffer 1; buffer 0 no longer read
-      if (t + 2 < n_iter) issue_tile(B0{}, t + 2);
-      do_tile(B1{}, t + 1);
-      if (t + 2 < n_iter) prescale_lse(B0{});
+  // Zero the tiles once, so rows past N (never copied) hold finite values.
+  {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = tid; i < BR * D / 8; i += kThreads) {
+      reinterpret_cast<u32x4_t*>(sQ0)[i] = z;
+      reinterpret_cast<u32x4_t*>(sQ1)[i] = z;
+      reinterpret_cast<u32x4_t*>(sdO0)[i] = z;
+      reinterpret_cast<u32x4_t*>(sdO1)[i] = z;
     }
+    if (tid < BR) {
+      sL0[tid] = sL1[tid] = sD0[tid] = sD1[tid] = 0.f;
+    }
+    __syncthreads();
+  }
+  Cursor cc{q_last, head0};  // tile being computed
+  Cursor ci = cc;            // tile being copied
+  {
+#pragma unroll
+    for (int k = 0; k < NDMA; ++k) copy_one(B0{}, ci, k);
+    prescale(B0{});
+  }
+  advance(ci);
+  auto tile = [&](auto bufc, int t) {
+    const bool masked = (CAUSAL && cc.q0 < k0 + BC) || ragged_keys || cc.q0 + BR > N;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile t in this buffer; the other buffer no longer read
+    // After the last tile the copy repeats the current tile into the idle
+    // buffer, which nothing reads: no branch around the copies.
+    do_tile(bufc, cc.q0, masked, t + 1 < n_iter ? ci : cc);
+    advance(ci);
+    advance(cc);
+  };
+  for (int t = 0; t < n_iter; t += 2) {
+    tile(B0{}, t);
+    if (t + 1 < n_iter) tile(B1{}, t + 1);
   }
 
-  // Epilogue: dK = tau * dK_acc, dV = dV_acc (rows = keys, lanes = d).
+  // Epilogue: dK = -tau * dK_acc (the accumulator holds -dS^T Q), dV = dV_acc
+  // (rows = keys, lanes = d).
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
 #pragma unroll
@@ -274,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       const int key = k0 + kw + 8 * (r >> 2) + 4 * g + (r & 3);
       if (key < N) {
         const int64_t off = (kv_off + key) * D + 32 * n + l32;
-        dK[off].bits = f32_to_bf16(dk_acc[n][r] * scale);
+        dK[off].bits = f32_to_bf16(dk_acc[n][r] * -scale);
         dV[off].bits = f32_to_bf16(dv_acc[n][r]);
       }
     }
