@@ -122,13 +122,13 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _params_from(q, k, causal, scale, softcap) -> attn_params:
+def _params_from(q, k, causal, scale, softcap, deterministic=False) -> attn_params:
     B, H, N, d = q.shape
     if k.dim() != 4 or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
         raise ValueError(f"K shape {tuple(k.shape)} does not match Q shape {tuple(q.shape)}")
     if k.dtype != q.dtype:
         raise TypeError("Q, K, V, O, dO must share one dtype")
-    return make_params(B, H, k.shape[1], N, d, _dtype_code(q), causal, scale, softcap)
+    return make_params(B, H, k.shape[1], N, d, _dtype_code(q), causal, scale, softcap, int(bool(deterministic)))
 
 
 def _check(status: int, where: str):
@@ -151,8 +151,9 @@ def attn_bwd_preprocess(o, do, D, dq_accum, *, H_kv=None, causal=False, scale=No
            "attn_bwd_preprocess")
 
 
-def attn_bwd(q, k, v, do, lse, D, dq_accum, dk, dv, *, causal=False, scale=None, softcap=0.0, stream=None):
-    p = _params_from(q, k, causal, scale, softcap)
+def attn_bwd(q, k, v, do, lse, D, dq_accum, dk, dv, *, causal=False, scale=None, softcap=0.0, stream=None,
+             deterministic=False):
+    p = _params_from(q, k, causal, scale, softcap, deterministic)
     lib = load_library()
     _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D),
                         _ptr(dq_accum), _ptr(dk), _ptr(dv), _stream(stream)), "attn_bwd")
@@ -177,9 +178,11 @@ def attention_forward(q, k, v, *, causal=False, scale=None, softcap=0.0, stream=
 
 
 def attention_backward(q, k, v, o, do, lse, *, causal=False, scale=None, softcap=0.0, stream=None,
-                       workspace=None):
+                       workspace=None, deterministic=False):
     """Returns (dQ, dK, dV): preprocess -> bwd -> dq_convert on one stream.
 
+    ``deterministic`` selects the atomic-free fp32 path (bf16 is atomic-free
+    either way).
     ``workspace`` may pass preallocated ``(D, dQaccum)`` fp32 tensors of shapes
     [B, H, N] and [B, H, N, d].
     """
@@ -194,6 +197,7 @@ def attention_backward(q, k, v, o, do, lse, *, causal=False, scale=None, softcap
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     attn_bwd_preprocess(o, do, D, acc, H_kv=k.shape[1], causal=causal, scale=scale, softcap=softcap, stream=stream)
-    attn_bwd(q, k, v, do, lse, D, acc, dk, dv, causal=causal, scale=scale, softcap=softcap, stream=stream)
+    attn_bwd(q, k, v, do, lse, D, acc, dk, dv, causal=causal, scale=scale, softcap=softcap, stream=stream,
+             deterministic=deterministic)
     attn_bwd_dq_convert(acc, dq, scale=scale if scale is not None else d ** -0.5, stream=stream)
     return dq, dk, dv

@@ -24,7 +24,7 @@ int check_params(const attn_params* p, fabwd::Problem* out, bool* empty) {
   if (p->causal != 0 && p->causal != 1) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(p->scale) || !(p->scale > 0.0f)) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(p->softcap) || p->softcap < 0.0f) return ATTN_ERR_INVALID_ARG;
-  if (p->deterministic != 0) return ATTN_ERR_UNSUPPORTED;
+  if (p->deterministic != 0 && p->deterministic != 1) return ATTN_ERR_INVALID_ARG;
   if (p->d != 64 && p->d != 128) return ATTN_ERR_UNSUPPORTED;
   if (p->N > kMaxN) return ATTN_ERR_INVALID_ARG;
   const int64_t elems = int64_t(p->B) * p->H * p->N * p->d;
@@ -38,6 +38,7 @@ int check_params(const attn_params* p, fabwd::Problem* out, bool* empty) {
   out->causal = p->causal != 0;
   out->scale = p->scale;
   out->softcap = p->softcap;
+  out->deterministic = p->deterministic != 0;
   *empty = (p->B == 0 || p->N == 0);
   return ATTN_OK;
 }

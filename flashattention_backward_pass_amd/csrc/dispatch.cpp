@@ -18,7 +18,11 @@ hipError_t launch_bwd(const Problem& p, const void* Q, const void* K, const void
     if (e != hipSuccess) return e;
     return launch_bwd_dq_mfma(p, Q, K, V, dO, LSE, D, dQacc, s);
   }
-  return launch_bwd_simple(p, Q, K, V, dO, LSE, D, dQacc, dK, dV, s);
+  // fp32: dQ partials added with atomics (the pages' scheme), or, in
+  // deterministic mode, dK/dV alone plus a query-block-outer dQ kernel.
+  hipError_t e = launch_bwd_simple(p, Q, K, V, dO, LSE, D, dQacc, dK, dV, s);
+  if (e != hipSuccess || !p.deterministic) return e;
+  return launch_bwd_dq_simple(p, Q, K, V, dO, LSE, D, dQacc, s);
 }
 
 }  // namespace fabwd

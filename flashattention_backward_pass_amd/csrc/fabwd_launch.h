@@ -14,6 +14,7 @@ struct Problem {
   bool causal;
   float scale;
   float softcap;
+  bool deterministic = false;  // fp32: no atomics (query-block-outer dQ kernel)
   int group() const { return H / H_kv; }
   int64_t q_rows() const { return int64_t(B) * H * N; }
   int64_t q_elems() const { return q_rows() * d; }
@@ -32,6 +33,8 @@ hipError_t launch_fwd_simple(const Problem& p, const void* Q, const void* K, con
                              hipStream_t s);
 hipError_t launch_bwd_simple(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                              const float* LSE, const float* D, float* dQacc, void* dK, void* dV, hipStream_t s);
+hipError_t launch_bwd_dq_simple(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                                const float* LSE, const float* Dv, float* dQacc, hipStream_t s);
 // bf16 matrix-core backward: dK/dV kernel (key blocks outer) and dQ kernel
 // (query blocks outer); the dQ kernel overwrites dQaccum.
 hipError_t launch_bwd_dkdv_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,

@@ -6,7 +6,8 @@
 // "解析 FlashAttention（3）：FlashAttention-v1 反向传播", section 4 (Algorithm 4):
 // key/value blocks outer, query blocks inner, P recomputed per tile from the
 // saved LSE (Inference Cookbook "反向传播算法详解", section 1.2), dK and dV kept
-// on chip, dQ partials added into an fp32 buffer (section 6.2 of the latter).
+// on chip, dQ partials added into an fp32 buffer (section 6.2 of the latter),
+// or, in deterministic mode, dQ from a query-block-outer kernel.
 //
 // Arithmetic: inputs are widened to fp32, every product and sum is fp32, and
 // exponentials are hardware exp2 with the log2(e) factor folded into the
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(const T* __restric
 // ----------------------------------------------------------------- backward
 // One workgroup per (key block of 32 keys, key/value head, batch); it loops
 // over the query heads of its group and over query blocks of 32 rows.
-template <typename T, int D, bool CAUSAL, bool SOFTCAP>
+template <typename T, int D, bool CAUSAL, bool SOFTCAP, bool ATOMIC_DQ>
 __global__ __launch_bounds__(kThreads) void bwd_simple_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                               const T* __restrict__ V, const T* __restrict__ dO,
                                                               const float* __restrict__ LSE,
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void bwd_simple_kernel(const T* __restric
         acc_dk[k] = ak;
       }
       // dQ partial of this (query block, key block) pair, unscaled.
-      if (row < N) {
+      if (ATOMIC_DQ && row < N) {
 #pragma unroll
         for (int k = 0; k < DX; ++k) {
           const int x = sub + 8 * k;
@@ -220,6 +221,89 @@ __global__ __launch_bounds__(kThreads) void bwd_simple_kernel(const T* __restric
   }
 }
 
+// ------------------------------------------------------- deterministic dQ
+// dQ_i = sum_j dS_ij K_j ("解析 FlashAttention（3）：FlashAttention-v1 反向传播",
+// eq (15), unscaled) with query blocks outer and key blocks inner: one
+// workgroup per (query block of 32 rows, head, batch) recomputes P and dS for
+// its rows and keeps dQ in registers; every sum runs in a fixed order and
+// dQaccum is written once with plain stores, so the result is bitwise
+// reproducible.  8 lanes per row, lane `sub` owns columns sub + 8k.
+template <typename T, int D, bool CAUSAL, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads) void bwd_dq_simple_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Dv, float* __restrict__ dQacc, int H, int H_kv, int N,
+    float scale, float softcap) {
+  constexpr int BQ = 32, BK = 32, DX = D / 8;
+  __shared__ float sQ[BQ][D + 1];
+  __shared__ float sdO[BQ][D + 1];
+  __shared__ float sK[BK][D + 1];
+  __shared__ float sV[BK][D + 1];
+  __shared__ float sdS[BQ][BK + 1];
+
+  const int t = threadIdx.x, r = t >> 3, sub = t & 7;
+  const int q0 = blockIdx.x * BQ, h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / (H / H_kv);
+  const int64_t q_off = (int64_t(b) * H + h) * N;
+  const int64_t kv_off = (int64_t(b) * H_kv + hk) * N * D;
+  const int row = q0 + r;
+
+  for (int idx = t; idx < BQ * D; idx += kThreads) {
+    const int rr = idx / D, x = idx % D;
+    const bool ok = q0 + rr < N;
+    sQ[rr][x] = ok ? Elem<T>::load(Q, (q_off + q0 + rr) * D + x) : 0.f;
+    sdO[rr][x] = ok ? Elem<T>::load(dO, (q_off + q0 + rr) * D + x) : 0.f;
+  }
+  const float lse2 = row < N ? LSE[q_off + row] * kLog2e : INFINITY;
+  const float dval = row < N ? Dv[q_off + row] : 0.f;
+  const float zscale = scale * kLog2e;
+  float acc[DX];
+#pragma unroll
+  for (int k = 0; k < DX; ++k) acc[k] = 0.f;
+
+  const int kv_end = CAUSAL ? min(N, q0 + BQ) : N;
+  for (int k0 = 0; k0 < kv_end; k0 += BK) {
+    __syncthreads();
+    for (int idx = t; idx < BK * D; idx += kThreads) {
+      const int kk = idx / D, x = idx % D;
+      const bool ok = k0 + kk < N;
+      sK[kk][x] = ok ? Elem<T>::load(K + kv_off, int64_t(k0 + kk) * D + x) : 0.f;
+      sV[kk][x] = ok ? Elem<T>::load(V + kv_off, int64_t(k0 + kk) * D + x) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < BK / 8; ++m) {
+      const int c = sub + 8 * m, key = k0 + c;
+      float s = 0.f, dp = 0.f;
+#pragma unroll 8
+      for (int x = 0; x < D; ++x) {
+        s = fmaf(sQ[r][x], sK[c][x], s);
+        dp = fmaf(sdO[r][x], sV[c][x], dp);
+      }
+      float dtanh = 1.f;
+      if (SOFTCAP) {
+        const float th = tanh_f32(s / softcap);
+        s = softcap * th;
+        dtanh = 1.f - th * th;
+      }
+      const bool masked = key >= N || row >= N || (CAUSAL && key > row);
+      const float p = masked ? 0.f : fast_exp2(s * zscale - lse2);
+      sdS[r][c] = p * (dp - dval) * dtanh;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < DX; ++k) {
+      const int x = sub + 8 * k;
+      float a = acc[k];
+      for (int c = 0; c < BK; ++c) a = fmaf(sdS[r][c], sK[c][x], a);
+      acc[k] = a;
+    }
+  }
+  if (row < N) {
+#pragma unroll
+    for (int k = 0; k < DX; ++k) dQacc[(q_off + row) * D + sub + 8 * k] = acc[k];
+  }
+}
+
 template <typename T, int D, bool C, bool S>
 hipError_t fwd_simple_t(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,
                         hipStream_t s) {
@@ -234,9 +318,20 @@ template <typename T, int D, bool C, bool S>
 hipError_t bwd_simple_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                         const float* LSE, const float* Dv, float* dQacc, void* dK, void* dV, hipStream_t s) {
   dim3 grid((p.N + 31) / 32, p.H_kv, p.B);
-  hipLaunchKernelGGL((bwd_simple_kernel<T, D, C, S>), grid, dim3(kThreads), 0, s, static_cast<const T*>(Q),
+  auto kern = p.deterministic ? bwd_simple_kernel<T, D, C, S, false> : bwd_simple_kernel<T, D, C, S, true>;
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, static_cast<const T*>(Q), static_cast<const T*>(K),
+                     static_cast<const T*>(V), static_cast<const T*>(dO), LSE, Dv, dQacc, static_cast<T*>(dK),
+                     static_cast<T*>(dV), p.H, p.H_kv, p.N, p.scale, p.softcap);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool C, bool S>
+hipError_t bwd_dq_simple_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                           const float* LSE, const float* Dv, float* dQacc, hipStream_t s) {
+  dim3 grid((p.N + 31) / 32, p.H, p.B);
+  hipLaunchKernelGGL((bwd_dq_simple_kernel<T, D, C, S>), grid, dim3(kThreads), 0, s, static_cast<const T*>(Q),
                      static_cast<const T*>(K), static_cast<const T*>(V), static_cast<const T*>(dO), LSE, Dv,
-                     dQacc, static_cast<T*>(dK), static_cast<T*>(dV), p.H, p.H_kv, p.N, p.scale, p.softcap);
+                     dQacc, p.H, p.H_kv, p.N, p.scale, p.softcap);
   return hipGetLastError();
 }
 
@@ -260,6 +355,16 @@ hipError_t bwd_simple_d(const Problem& p, const void* Q, const void* K, const vo
             : bwd_simple_t<T, D, false, false>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s);
 }
 
+template <typename T, int D>
+hipError_t bwd_dq_simple_d(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                           const float* LSE, const float* Dv, float* dQacc, hipStream_t s) {
+  const bool sc = p.softcap > 0.f;
+  if (p.causal) return sc ? bwd_dq_simple_t<T, D, true, true>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
+                          : bwd_dq_simple_t<T, D, true, false>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
+  return sc ? bwd_dq_simple_t<T, D, false, true>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
+            : bwd_dq_simple_t<T, D, false, false>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
+}
+
 }  // namespace
 
 hipError_t launch_fwd_simple(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,
@@ -278,6 +383,19 @@ hipError_t launch_bwd_simple(const Problem& p, const void* Q, const void* K, con
                      : bwd_simple_d<bf16_t, 128>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s);
   return p.d == 64 ? bwd_simple_d<float, 64>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s)
                    : bwd_simple_d<float, 128>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s);
+}
+
+}  // namespace fabwd
+
+namespace fabwd {
+
+hipError_t launch_bwd_dq_simple(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                                const float* LSE, const float* Dv, float* dQacc, hipStream_t s) {
+  if (p.dtype == 1)
+    return p.d == 64 ? bwd_dq_simple_d<bf16_t, 64>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
+                     : bwd_dq_simple_d<bf16_t, 128>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
+  return p.d == 64 ? bwd_dq_simple_d<float, 64>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
+                   : bwd_dq_simple_d<float, 128>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
 }
 
 }  // namespace fabwd

@@ -61,7 +61,7 @@ typedef struct attn_params {
   int32_t causal;           /* 0 or 1 */
   float scale;              /* softmax scale tau, finite and > 0 (usually 1/sqrt(d)) */
   float softcap;            /* c > 0 enables the tanh cap, 0 disables it */
-  int32_t deterministic;    /* reserved, must be 0 */
+  int32_t deterministic;    /* 0 or 1; see attn_bwd */
 } attn_params;
 
 /* Supported head dimensions: d = 64 and d = 128, for both dtypes. */
@@ -102,9 +102,16 @@ int attn_bwd_preprocess(const attn_params* p, const void* O, const void* dO,
  *         query-block-outer kernel that recomputes S and dP and keeps dQ in
  *         registers; every row of dQaccum is overwritten with plain stores,
  *         so the result is bitwise reproducible (no atomics).
- *   fp32: one kernel adds the dQ partials of each key block into the zeroed
- *         dQaccum with fp32 atomics; the order of those additions is not
- *         fixed, so the low bits of dQ may differ between runs.
+ *   fp32, deterministic = 0: one kernel adds the dQ partials of each key
+ *         block into the zeroed dQaccum with fp32 atomics ([CB] 6.2); the
+ *         order of those additions is not fixed, so the low bits of dQ may
+ *         differ between runs.
+ *   fp32, deterministic = 1: the deterministic mode of [CB] 6.4: dK/dV from
+ *         the same kernel without the atomics, and dQaccum overwritten by a
+ *         query-block-outer kernel that sums in a fixed order; bitwise
+ *         reproducible.
+ * The bf16 path is reproducible for either value of `deterministic`.
+ * Errors: ATTN_ERR_INVALID_ARG for deterministic other than 0 or 1.
  */
 int attn_bwd(const attn_params* p, const void* Q, const void* K, const void* V,
              const void* dO, const float* LSE, const float* D,

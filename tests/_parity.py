@@ -25,7 +25,7 @@ def to_np(t):
     return t.detach().double().cpu().numpy()
 
 
-def run_gpu(w, x, *, o=None, lse=None, poison=False):
+def run_gpu(w, x, *, o=None, lse=None, poison=False, deterministic=False):
     """Forward (unless o/lse given) then backward on cuda:0.  Returns numpy dict."""
     dev = torch.device("cuda:0")
     q, k, v, do = (x[n].to(dev) for n in ("Q", "K", "V", "dO"))
@@ -41,7 +41,8 @@ def run_gpu(w, x, *, o=None, lse=None, poison=False):
         for t in (D, acc, dq, dk, dv):
             t.fill_(float("nan"))
     fab.attn_bwd_preprocess(o, do, D, acc, H_kv=w.H_kv, causal=w.causal, scale=w.tau, softcap=w.softcap)
-    fab.attn_bwd(q, k, v, do, lse, D, acc, dk, dv, causal=w.causal, scale=w.tau, softcap=w.softcap)
+    fab.attn_bwd(q, k, v, do, lse, D, acc, dk, dv, causal=w.causal, scale=w.tau, softcap=w.softcap,
+                 deterministic=deterministic)
     acc_copy = acc.clone()
     fab.attn_bwd_dq_convert(acc, dq, scale=w.tau)
     torch.cuda.synchronize()

@@ -94,8 +94,15 @@ def test_unsupported_head_dim(lib, d):
     assert call_all(lib, fab.make_params(1, 2, 2, 64, d, 1)) == [fab.ATTN_ERR_UNSUPPORTED] * 4
 
 
-def test_deterministic_mode_unsupported(lib):
-    assert call_all(lib, fab.make_params(1, 2, 2, 64, 64, 1, deterministic=1)) == [fab.ATTN_ERR_UNSUPPORTED] * 4
+@pytest.mark.parametrize("det", [2, -1])
+def test_deterministic_flag_out_of_range(lib, det):
+    assert call_all(lib, fab.make_params(1, 2, 2, 64, 64, 1, deterministic=det)) == [fab.ATTN_ERR_INVALID_ARG] * 4
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_deterministic_mode_accepted(lib, dtype):
+    # An empty problem validates every argument but launches nothing.
+    assert call_all(lib, fab.make_params(1, 2, 2, 0, 64, dtype, deterministic=1), ptr=None) == [fab.ATTN_OK] * 4
 
 
 def test_null_params(lib):
