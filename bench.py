@@ -162,6 +162,17 @@ def main():
     bwd = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     cvt = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
 
+    # The forward (attn_fwd_stats) is a support step outside the timed
+    # backward step; timed here on its own for reference.
+    fe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    fe[0].record()
+    for _ in range(5):
+        fab.attn_fwd_stats(q, k, v, o, lse, **kw)
+    fe[1].record()
+    torch.cuda.synchronize()
+    fwd_ms = fe[0].elapsed_time(fe[1]) / 5
+    fwd_flops = 4.0 * B * H * N * N * d / (2.0 if w.causal else 1.0)
+
     flops = w.flops()
     ms = wall / args.steps * 1e3
     value = flops / (ms * 1e-3) / 1e12
@@ -197,6 +208,8 @@ def main():
         "stream_kernels_GBs": {"bwd_preprocess": round(pre_bytes / (pre * 1e-3) / 1e9, 1),
                                "bwd_dq_convert": round(cvt_bytes / (cvt * 1e-3) / 1e9, 1),
                                "peak": PEAK_HBM_GBS},
+        "forward": {"kernel": "attn_fwd_stats (not part of the timed step)", "ms": round(fwd_ms, 4),
+                    "tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 1), "flops": "4 N^2 d per head, halved when causal"},
     }
     try:
         out["git"] = subprocess.run(["git", "rev-parse", "--short", "HEAD"], capture_output=True, text=True,

@@ -6,6 +6,8 @@ namespace fabwd {
 hipError_t launch_fwd_stats(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,
                             hipStream_t s) {
   (void)hipGetLastError();
+  // bf16: matrix-core kernel; fp32: vector-ALU kernel.
+  if (p.dtype == 1) return launch_fwd_mfma(p, Q, K, V, O, LSE, s);
   return launch_fwd_simple(p, Q, K, V, O, LSE, s);
 }
 

@@ -31,6 +31,8 @@ hipError_t launch_bwd_dq_convert(const Problem& p, const float* dQacc, void* dQ,
 // Kernel families behind launch_fwd_stats / launch_bwd (dispatch.cpp picks one).
 hipError_t launch_fwd_simple(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,
                              hipStream_t s);
+hipError_t launch_fwd_mfma(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                           hipStream_t s);
 hipError_t launch_bwd_simple(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                              const float* LSE, const float* D, float* dQacc, void* dK, void* dV, hipStream_t s);
 hipError_t launch_bwd_dq_simple(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
