@@ -20,7 +20,9 @@ Z = tau * (capped score) are the softmax logits ([FA1] 2.5 writes S = tau Q K^T
 when there is no cap).  P = softmax(Z) row-wise, O = P V, LSE_i = ln sum_j
 exp(Z_ij) ([CB] 1.2).  Causal masking sets Z_ij = -inf for key j > query i
 (the diagonal is kept), after the cap ([CB] 5.2 step 3 applies the cap before
-the mask).
+the mask).  A local (sliding-window) mask with window (wl, wr) also sets
+Z_ij = -inf for j < i - wl (when wl >= 0) and for j > i + wr (when wr >= 0);
+-1 leaves that side unbounded.
 
 Readings taken where the pages are silent or ambiguous:
   * the cap applies to the unscaled scores R, and tau multiplies the capped
@@ -29,7 +31,11 @@ Readings taken where the pages are silent or ambiguous:
   * the dPsum of [CB] 2.1 is D_i = sum_k dO_ik O_ik ([FA1] eq (6));
   * grouped-query attention: query head h reads key/value head h // G with
     G = H / H_kv, and dK, dV of a key/value head sum over its G query heads
-    ([CB] 8.5).
+    ([CB] 8.5);
+  * the local mask: the backward-kernel page names a third masking phase for
+    the query blocks at a local window's boundary but gives no formula; the
+    window is read as the band i - wl <= j <= i + wr around the diagonal,
+    combined with the causal mask when both are on.
 
 Parity pins: tests/test_oracle_*.py (N=2, d=2 hand expansions of [FA1]
 section 2, central finite differences of <dO, O>, invariants, closed forms,
@@ -61,12 +67,28 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def _logits(q, k, q_idx, k_idx, tau, causal, softcap):
+def _visible(q_idx, k_idx, causal, window):
+    """Boolean [len(q_idx), len(k_idx)]: key j is visible to query i."""
+    i = q_idx[:, None]
+    j = k_idx[None, :]
+    ok = np.ones((q_idx.size, k_idx.size), dtype=bool)
+    if causal:
+        ok &= j <= i
+    wl, wr = window if window is not None else (-1, -1)
+    if wl >= 0:
+        ok &= j >= i - wl
+    if wr >= 0:
+        ok &= j <= i + wr
+    return ok
+
+
+def _logits(q, k, q_idx, k_idx, tau, causal, softcap, window=None):
     """Logits Z (rows q_idx, columns k_idx) and T = tanh(R/c) (None if no cap).
 
     R = q K^T ([CB] 1.1); capped score c*tanh(R/c) ([CB] 2.1 (3));
-    Z = tau * capped score; causal: Z_ij = -inf for j > i ([FA1] section 4,
-    the mask step of Algorithm 4 sets masked scores to -inf).
+    Z = tau * capped score; masked entries (causal: j > i; local window: outside
+    i - wl <= j <= i + wr) are -inf ([FA1] section 4, the mask step of
+    Algorithm 4 sets masked scores to -inf).
     """
     R = q @ k.T
     if softcap > 0.0:
@@ -75,13 +97,12 @@ def _logits(q, k, q_idx, k_idx, tau, causal, softcap):
     else:
         T = None
         Z = tau * R
-    if causal:
-        masked = k_idx[None, :] > q_idx[:, None]
-        Z = np.where(masked, -np.inf, Z)
+    if causal or (window is not None and tuple(window) != (-1, -1)):
+        Z = np.where(_visible(q_idx, k_idx, causal, window), Z, -np.inf)
     return Z, T
 
 
-def forward_rows_head(q, k, v, rows, tau, causal=False, softcap=0.0):
+def forward_rows_head(q, k, v, rows, tau, causal=False, softcap=0.0, window=None):
     """O and LSE of the query rows `rows` of one head, straight from the definition.
 
     q: [N, d], k, v: [N, d].  P_i = softmax(Z_i) ([FA1] 1.1), O_i = P_i V,
@@ -92,20 +113,20 @@ def forward_rows_head(q, k, v, rows, tau, causal=False, softcap=0.0):
     rows = np.asarray(rows, dtype=np.int64)
     if rows.size == 0:
         return np.zeros((0, v.shape[1])), np.zeros((0,))
-    Z, _ = _logits(q[rows], k, rows, np.arange(k.shape[0]), tau, causal, softcap)
+    Z, _ = _logits(q[rows], k, rows, np.arange(k.shape[0]), tau, causal, softcap, window)
     m = Z.max(axis=1)
     lse = m + np.log(np.exp(Z - m[:, None]).sum(axis=1))
     P = np.exp(Z - lse[:, None])
     return P @ v, lse
 
 
-def forward_head(q, k, v, tau, causal=False, softcap=0.0):
+def forward_head(q, k, v, tau, causal=False, softcap=0.0, window=None):
     """O [N, d] and LSE [N] of one head (all rows)."""
     n = _f64(q).shape[0]
-    return forward_rows_head(q, k, v, np.arange(n), tau, causal, softcap)
+    return forward_rows_head(q, k, v, np.arange(n), tau, causal, softcap, window)
 
 
-def backward_head(q, k, v, o, do, lse, tau, causal=False, softcap=0.0):
+def backward_head(q, k, v, o, do, lse, tau, causal=False, softcap=0.0, window=None):
     """dQ, dK, dV [N, d] and D [N] of one head from the saved forward tensors.
 
     Inputs are what [CB] 1.3 says the forward saves (Q, K, V, O, LSE) plus dO.
@@ -123,7 +144,7 @@ def backward_head(q, k, v, o, do, lse, tau, causal=False, softcap=0.0):
         z = np.zeros((0, q.shape[1]))
         return z, np.zeros_like(_f64(k)), np.zeros_like(_f64(v)), np.zeros((0,))
     idx = np.arange(n)
-    Z, T = _logits(q, k, idx, np.arange(k.shape[0]), tau, causal, softcap)
+    Z, T = _logits(q, k, idx, np.arange(k.shape[0]), tau, causal, softcap, window)
     P = np.exp(Z - lse[:, None])
     del Z
     dV = P.T @ do
@@ -141,7 +162,7 @@ def backward_head(q, k, v, o, do, lse, tau, causal=False, softcap=0.0):
     return dQ, dK, dV, D
 
 
-def backward_q_rows_head(q, k, v, o_rows, do_rows, lse_rows, rows, tau, causal=False, softcap=0.0):
+def backward_q_rows_head(q, k, v, o_rows, do_rows, lse_rows, rows, tau, causal=False, softcap=0.0, window=None):
     """dQ and D of the query rows `rows` of one head.
 
     Row i of dQ needs only row i of P, dP and D: dQ_i = sum_j dR_ij K_j
@@ -153,7 +174,7 @@ def backward_q_rows_head(q, k, v, o_rows, do_rows, lse_rows, rows, tau, causal=F
     rows = np.asarray(rows, dtype=np.int64)
     if rows.size == 0:
         return np.zeros((0, q.shape[1])), np.zeros((0,))
-    Z, T = _logits(q[rows], k, rows, np.arange(k.shape[0]), tau, causal, softcap)
+    Z, T = _logits(q[rows], k, rows, np.arange(k.shape[0]), tau, causal, softcap, window)
     P = np.exp(Z - lse_rows[:, None])
     dP = do_rows @ v.T
     D = (do_rows * o_rows).sum(axis=1)
@@ -162,7 +183,7 @@ def backward_q_rows_head(q, k, v, o_rows, do_rows, lse_rows, rows, tau, causal=F
     return dR @ k, D
 
 
-def backward_kv_rows_head(q, k, v, o, do, lse, kv_rows, tau, causal=False, softcap=0.0):
+def backward_kv_rows_head(q, k, v, o, do, lse, kv_rows, tau, causal=False, softcap=0.0, window=None):
     """dK and dV of the key rows `kv_rows` contributed by one query head.
 
     Column j of P, dP and dZ over all query rows gives
@@ -173,7 +194,7 @@ def backward_kv_rows_head(q, k, v, o, do, lse, kv_rows, tau, causal=False, softc
     cols = np.asarray(kv_rows, dtype=np.int64)
     if cols.size == 0:
         return np.zeros((0, k.shape[1])), np.zeros((0, v.shape[1]))
-    Zc, Tc = _logits(q, k[cols], np.arange(q.shape[0]), cols, tau, causal, softcap)
+    Zc, Tc = _logits(q, k[cols], np.arange(q.shape[0]), cols, tau, causal, softcap, window)
     Pc = np.exp(Zc - lse[:, None])
     dPc = do @ v[cols].T
     D = (do * o).sum(axis=1)
@@ -188,7 +209,7 @@ def _group(H, H_kv):
     return H // H_kv
 
 
-def forward(Q, K, V, tau, causal=False, softcap=0.0):
+def forward(Q, K, V, tau, causal=False, softcap=0.0, window=None):
     """O [B,H,N,d] and LSE [B,H,N] for Q [B,H,N,d], K, V [B,H_kv,N,d].
 
     Query head h reads key/value head h // (H / H_kv) ([CB] 8.5).
@@ -200,11 +221,11 @@ def forward(Q, K, V, tau, causal=False, softcap=0.0):
     LSE = np.zeros((B, H, N))
     for b in range(B):
         for h in range(H):
-            O[b, h], LSE[b, h] = forward_head(Q[b, h], K[b, h // G], V[b, h // G], tau, causal, softcap)
+            O[b, h], LSE[b, h] = forward_head(Q[b, h], K[b, h // G], V[b, h // G], tau, causal, softcap, window)
     return O, LSE
 
 
-def backward(Q, K, V, O, dO, LSE, tau, causal=False, softcap=0.0):
+def backward(Q, K, V, O, dO, LSE, tau, causal=False, softcap=0.0, window=None):
     """dQ [B,H,N,d], dK, dV [B,H_kv,N,d], D [B,H,N] from the saved tensors.
 
     dK and dV of key/value head g sum the contributions of its G query heads
@@ -221,7 +242,7 @@ def backward(Q, K, V, O, dO, LSE, tau, causal=False, softcap=0.0):
         for h in range(H):
             g = h // G
             dq, dk, dv, dd = backward_head(Q[b, h], K[b, g], V[b, g], O[b, h], dO[b, h], LSE[b, h],
-                                           tau, causal, softcap)
+                                           tau, causal, softcap, window)
             dQ[b, h] = dq
             dK[b, g] += dk
             dV[b, g] += dv
@@ -229,8 +250,10 @@ def backward(Q, K, V, O, dO, LSE, tau, causal=False, softcap=0.0):
     return dQ, dK, dV, D
 
 
-def reference(Q, K, V, dO, tau, causal=False, softcap=0.0):
-    """Forward then backward in fp64: dict with O, LSE, D, dQ, dK, dV."""
-    O, LSE = forward(Q, K, V, tau, causal, softcap)
-    dQ, dK, dV, D = backward(Q, K, V, O, dO, LSE, tau, causal, softcap)
+def reference(Q, K, V, dO, tau, causal=False, softcap=0.0, window=None):
+    """Forward then backward in fp64: dict with O, LSE, D, dQ, dK, dV.
+
+    window = (wl, wr) adds the local mask (-1: that side unbounded)."""
+    O, LSE = forward(Q, K, V, tau, causal, softcap, window)
+    dQ, dK, dV, D = backward(Q, K, V, O, dO, LSE, tau, causal, softcap, window)
     return {"O": O, "LSE": LSE, "D": D, "dQ": dQ, "dK": dK, "dV": dV}

@@ -21,8 +21,10 @@ MUTATIONS = {
     "untransposed_P_in_dV": ("dV = P.T @ do", "dV = P @ do"),
     "missing_tau_on_dR": ("        dR = tau * dZ\n", "        dR = dZ\n"),
     "softcap_derivative_sign": ("dR = tau * dZ * (1.0 - T * T)", "dR = tau * dZ * (1.0 + T * T)"),
-    "mask_direction": ("k_idx[None, :] > q_idx[:, None]", "k_idx[None, :] < q_idx[:, None]"),
-    "mask_drops_diagonal": ("k_idx[None, :] > q_idx[:, None]", "k_idx[None, :] >= q_idx[:, None]"),
+    "mask_direction": ("ok &= j <= i\n", "ok &= j >= i\n"),
+    "mask_drops_diagonal": ("ok &= j <= i\n", "ok &= j < i\n"),
+    "window_left_off_by_one": ("ok &= j >= i - wl", "ok &= j > i - wl"),
+    "window_right_mirrored": ("ok &= j <= i + wr", "ok &= j <= i - wr"),
     "lse_without_max": ("lse = m + np.log(", "lse = np.log("),
     "gqa_head_map": ("            g = h // G\n", "            g = h % K.shape[1]\n"),
     "dK_against_K": ("dK = dR.T @ q", "dK = dR.T @ k"),
@@ -93,7 +95,38 @@ def pin_softcap_identity(mod):
     return bool(ok and all(np.allclose(a[n], b[n], atol=1e-8) for n in ("O", "dQ", "dK", "dV")))
 
 
-PINS = (pin_finite_differences, pin_torch_sdpa, pin_softcap_identity)
+def pin_window(mod):
+    """Local window: fp64 autograd of torch's scaled_dot_product_attention with
+    the band written out as a boolean mask, and window (0, 0) in closed form
+    (each query sees only its own key: O = V, dQ = dK = 0, dV = dO)."""
+    B, H, N, d = 1, 2, 11, 4
+    g = torch.Generator().manual_seed(2)
+    Q, K, V, dO = (torch.randn(B, H, N, d, generator=g, dtype=torch.float64) for _ in range(4))
+    i = torch.arange(N)[:, None]
+    j = torch.arange(N)[None, :]
+    ok = True
+    for causal, (wl, wr) in ((False, (3, 2)), (True, (4, -1)), (False, (-1, 1))):
+        band = torch.ones(N, N, dtype=torch.bool)
+        if causal:
+            band &= j <= i
+        if wl >= 0:
+            band &= j >= i - wl
+        if wr >= 0:
+            band &= j <= i + wr
+        q, k, v = (t.clone().requires_grad_(True) for t in (Q, K, V))
+        out = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=band, scale=0.7)
+        out.backward(dO)
+        r = mod.reference(Q, K, V, dO, 0.7, causal, 0.0, (wl, wr))
+        ok = ok and np.allclose(r["O"], out.detach().numpy(), atol=1e-10)
+        for n, t in (("dQ", q), ("dK", k), ("dV", v)):
+            ok = ok and np.allclose(r[n], t.grad.numpy(), atol=1e-10)
+    r = mod.reference(Q, K, V, dO, 0.7, False, 0.0, (0, 0))
+    ok = ok and np.allclose(r["O"], V.numpy(), atol=1e-12) and np.allclose(r["dV"], dO.numpy(), atol=1e-12)
+    ok = ok and np.abs(r["dQ"]).max() < 1e-12 and np.abs(r["dK"]).max() < 1e-12
+    return bool(ok)
+
+
+PINS = (pin_finite_differences, pin_torch_sdpa, pin_softcap_identity, pin_window)
 
 
 def test_unmutated_source_passes_every_pin():

@@ -320,3 +320,22 @@ def test_rows_match_full(causal, softcap):
     dkr, dvr = oracle.backward_kv_rows_head(q, k, v, O, do, L, rows, tau, causal, softcap)
     np.testing.assert_allclose(dkr, dk[rows], atol=1e-14)
     np.testing.assert_allclose(dvr, dv[rows], atol=1e-14)
+
+
+def test_window_invariants():
+    """A window at least N wide on both sides masks nothing; causal equals
+    the window (-1, 0); a window only narrows what a query sees."""
+    rng = np.random.default_rng(21)
+    B, H, N, d = 1, 2, 9, 4
+    Q, K, V, dO = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    plain = oracle.reference(Q, K, V, dO, 0.5, False, 0.0)
+    wide = oracle.reference(Q, K, V, dO, 0.5, False, 0.0, (N, N))
+    for n in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.allclose(plain[n], wide[n], atol=1e-12), n
+    causal = oracle.reference(Q, K, V, dO, 0.5, True, 0.0)
+    band = oracle.reference(Q, K, V, dO, 0.5, False, 0.0, (-1, 0))
+    for n in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.allclose(causal[n], band[n], atol=1e-12), n
+    # LSE is a log-sum-exp over the visible keys: a narrower window cannot raise it.
+    narrow = oracle.reference(Q, K, V, dO, 0.5, True, 0.0, (2, -1))
+    assert np.all(narrow["LSE"] <= causal["LSE"] + 1e-12)
