@@ -97,10 +97,10 @@ def cpu_baseline(w, x, heads=3):
     for h in range(heads):
         q, do = x["Q"][0, h], x["dO"][0, h]
         k, v = x["K"][0, h // group], x["V"][0, h // group]
-        O, L = oracle.forward_head(q, k, v, w.tau, w.causal, w.softcap)
-        oracle.backward_head(q, k, v, O, do, L, w.tau, w.causal, w.softcap)
+        O, L = oracle.forward_head(q, k, v, w.tau, w.causal, w.softcap, w.window)
+        oracle.backward_head(q, k, v, O, do, L, w.tau, w.causal, w.softcap, w.window)
     dt = time.perf_counter() - t0
-    flops = heads * 10.0 * w.N * w.N * w.d / (2.0 if w.causal else 1.0)
+    flops = heads * w.flops() / (w.B * w.H)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"{heads} query heads (b=0, h=0..{heads - 1}) of the workload at full N={w.N}: "
                       f"fp64 forward + backward, {dt:.1f} s wall; metric FLOPs of those heads",
@@ -126,7 +126,7 @@ def main():
     x = workloads.make_inputs(w)
     dev = torch.device("cuda:0")
     q, k, v, do = (x[n].to(dev) for n in ("Q", "K", "V", "dO"))
-    kw = dict(causal=w.causal, scale=w.tau, softcap=w.softcap)
+    kw = dict(causal=w.causal, scale=w.tau, softcap=w.softcap, window=w.window)
     o, lse = fab.attention_forward(q, k, v, **kw)
     B, H, N, d = q.shape
     D = torch.empty(B, H, N, device=dev, dtype=torch.float32)
@@ -171,7 +171,7 @@ def main():
     fe[1].record()
     torch.cuda.synchronize()
     fwd_ms = fe[0].elapsed_time(fe[1]) / 5
-    fwd_flops = 4.0 * B * H * N * N * d / (2.0 if w.causal else 1.0)
+    fwd_flops = 0.4 * w.flops()  # 4 N^2 d per head (causal: half; window: 4 d per visible pair)
 
     flops = w.flops()
     ms = wall / args.steps * 1e3
@@ -201,15 +201,15 @@ def main():
                      "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "attn_bwd entry point (bf16: bwd_dkdv_kernel + bwd_dq_kernel)",
                      "flops_per_launch": flops,
-                     "note": "achieved = metric FLOPs (10 N^2 d per head, halved when causal) / measured attn_bwd "
-                             "time; the two kernels issue 14 N^2 d (halved) of MFMA work because the dQ kernel "
-                             "recomputes S and dP"},
+                     "note": "achieved = metric FLOPs (10 N^2 d per head, halved when causal; with a local window "
+                             "10 d per visible (query, key) pair) / measured attn_bwd time; the two kernels issue "
+                             "14/10 of that as MFMA work because the dQ kernel recomputes S and dP"},
         "kernels_ms": {"bwd_preprocess": round(pre, 4), "bwd": round(bwd, 4), "bwd_dq_convert": round(cvt, 4)},
         "stream_kernels_GBs": {"bwd_preprocess": round(pre_bytes / (pre * 1e-3) / 1e9, 1),
                                "bwd_dq_convert": round(cvt_bytes / (cvt * 1e-3) / 1e9, 1),
                                "peak": PEAK_HBM_GBS},
         "forward": {"kernel": "attn_fwd_stats (not part of the timed step)", "ms": round(fwd_ms, 4),
-                    "tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 1), "flops": "4 N^2 d per head, halved when causal"},
+                    "tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 1), "flops": "4/10 of the backward metric FLOPs"},
     }
     try:
         out["git"] = subprocess.run(["git", "rev-parse", "--short", "HEAD"], capture_output=True, text=True,

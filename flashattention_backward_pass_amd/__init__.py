@@ -48,6 +48,8 @@ class attn_params(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("softcap", ctypes.c_float),
         ("deterministic", ctypes.c_int32),
+        ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
     ]
 
 
@@ -82,11 +84,14 @@ def status_str(status: int) -> str:
     return load_library().attn_status_str(int(status)).decode()
 
 
-def make_params(B, H, H_kv, N, d, dtype, causal=False, scale=None, softcap=0.0, deterministic=0) -> attn_params:
+def make_params(B, H, H_kv, N, d, dtype, causal=False, scale=None, softcap=0.0, deterministic=0,
+                window=None) -> attn_params:
+    """window = (window_left, window_right) local mask, -1 = unbounded side; None = no window."""
     if scale is None:
         scale = d ** -0.5
+    wl, wr = (-1, -1) if window is None else window
     return attn_params(int(B), int(H), int(H_kv), int(N), int(d), int(dtype), int(bool(causal)),
-                       float(scale), float(softcap), int(deterministic))
+                       float(scale), float(softcap), int(deterministic), int(wl), int(wr))
 
 
 # ------------------------------------------------------------ torch marshalling
@@ -122,13 +127,14 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _params_from(q, k, causal, scale, softcap, deterministic=False) -> attn_params:
+def _params_from(q, k, causal, scale, softcap, deterministic=False, window=None) -> attn_params:
     B, H, N, d = q.shape
     if k.dim() != 4 or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
         raise ValueError(f"K shape {tuple(k.shape)} does not match Q shape {tuple(q.shape)}")
     if k.dtype != q.dtype:
         raise TypeError("Q, K, V, O, dO must share one dtype")
-    return make_params(B, H, k.shape[1], N, d, _dtype_code(q), causal, scale, softcap, int(bool(deterministic)))
+    return make_params(B, H, k.shape[1], N, d, _dtype_code(q), causal, scale, softcap, int(bool(deterministic)),
+                       window)
 
 
 def _check(status: int, where: str):
@@ -136,24 +142,25 @@ def _check(status: int, where: str):
         raise AttnError(status, where)
 
 
-def attn_fwd_stats(q, k, v, o, lse, *, causal=False, scale=None, softcap=0.0, stream=None):
-    p = _params_from(q, k, causal, scale, softcap)
+def attn_fwd_stats(q, k, v, o, lse, *, causal=False, scale=None, softcap=0.0, stream=None, window=None):
+    p = _params_from(q, k, causal, scale, softcap, window=window)
     lib = load_library()
     _check(lib.attn_fwd_stats(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(stream)),
            "attn_fwd_stats")
 
 
-def attn_bwd_preprocess(o, do, D, dq_accum, *, H_kv=None, causal=False, scale=None, softcap=0.0, stream=None):
+def attn_bwd_preprocess(o, do, D, dq_accum, *, H_kv=None, causal=False, scale=None, softcap=0.0, stream=None,
+                        window=None):
     B, H, N, d = o.shape
-    p = make_params(B, H, H_kv or H, N, d, _dtype_code(o), causal, scale, softcap)
+    p = make_params(B, H, H_kv or H, N, d, _dtype_code(o), causal, scale, softcap, window=window)
     lib = load_library()
     _check(lib.attn_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(do), _ptr(D), _ptr(dq_accum), _stream(stream)),
            "attn_bwd_preprocess")
 
 
 def attn_bwd(q, k, v, do, lse, D, dq_accum, dk, dv, *, causal=False, scale=None, softcap=0.0, stream=None,
-             deterministic=False):
-    p = _params_from(q, k, causal, scale, softcap, deterministic)
+             deterministic=False, window=None):
+    p = _params_from(q, k, causal, scale, softcap, deterministic, window)
     lib = load_library()
     _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D),
                         _ptr(dq_accum), _ptr(dk), _ptr(dv), _stream(stream)), "attn_bwd")
@@ -167,18 +174,18 @@ def attn_bwd_dq_convert(dq_accum, dq, *, scale=None, stream=None):
            "attn_bwd_dq_convert")
 
 
-def attention_forward(q, k, v, *, causal=False, scale=None, softcap=0.0, stream=None):
+def attention_forward(q, k, v, *, causal=False, scale=None, softcap=0.0, stream=None, window=None):
     """Returns (O, LSE) from attn_fwd_stats."""
     torch = _torch()
     B, H, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
-    attn_fwd_stats(q, k, v, o, lse, causal=causal, scale=scale, softcap=softcap, stream=stream)
+    attn_fwd_stats(q, k, v, o, lse, causal=causal, scale=scale, softcap=softcap, stream=stream, window=window)
     return o, lse
 
 
 def attention_backward(q, k, v, o, do, lse, *, causal=False, scale=None, softcap=0.0, stream=None,
-                       workspace=None, deterministic=False):
+                       workspace=None, deterministic=False, window=None):
     """Returns (dQ, dK, dV): preprocess -> bwd -> dq_convert on one stream.
 
     ``deterministic`` selects the atomic-free fp32 path (bf16 is atomic-free
@@ -196,8 +203,9 @@ def attention_backward(q, k, v, o, do, lse, *, causal=False, scale=None, softcap
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    attn_bwd_preprocess(o, do, D, acc, H_kv=k.shape[1], causal=causal, scale=scale, softcap=softcap, stream=stream)
+    attn_bwd_preprocess(o, do, D, acc, H_kv=k.shape[1], causal=causal, scale=scale, softcap=softcap, stream=stream,
+                        window=window)
     attn_bwd(q, k, v, do, lse, D, acc, dk, dv, causal=causal, scale=scale, softcap=softcap, stream=stream,
-             deterministic=deterministic)
+             deterministic=deterministic, window=window)
     attn_bwd_dq_convert(acc, dq, scale=scale if scale is not None else d ** -0.5, stream=stream)
     return dq, dk, dv

@@ -2,6 +2,7 @@
 // Declarations and the contract of every entry point: include/fabwd.h.
 #include "../../include/fabwd.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -25,6 +26,7 @@ int check_params(const attn_params* p, fabwd::Problem* out, bool* empty) {
   if (!std::isfinite(p->scale) || !(p->scale > 0.0f)) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(p->softcap) || p->softcap < 0.0f) return ATTN_ERR_INVALID_ARG;
   if (p->deterministic != 0 && p->deterministic != 1) return ATTN_ERR_INVALID_ARG;
+  if (p->window_left < -1 || p->window_right < -1) return ATTN_ERR_INVALID_ARG;
   if (p->d != 64 && p->d != 128) return ATTN_ERR_UNSUPPORTED;
   if (p->N > kMaxN) return ATTN_ERR_INVALID_ARG;
   const int64_t elems = int64_t(p->B) * p->H * p->N * p->d;
@@ -39,6 +41,13 @@ int check_params(const attn_params* p, fabwd::Problem* out, bool* empty) {
   out->scale = p->scale;
   out->softcap = p->softcap;
   out->deterministic = p->deterministic != 0;
+  {
+    const int n = p->N;
+    out->wl = p->window_left < 0 ? n : std::min(p->window_left, n);
+    int wr = p->window_right < 0 ? n : std::min(p->window_right, n);
+    if (p->causal) wr = std::min(wr, 0);
+    out->wr = wr;
+  }
   *empty = (p->B == 0 || p->N == 0);
   return ATTN_OK;
 }

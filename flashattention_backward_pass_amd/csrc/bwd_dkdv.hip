@@ -58,12 +58,14 @@ struct Cursor {
   int64_t row0;  // (b*H + h)*N, row offset of the query head
 };
 
-template <int D, bool CAUSAL, bool SOFTCAP>
+// Key k is visible to query q iff q - wl <= k <= q + wr and k < N (causal:
+// wr = 0; an unbounded side is N).
+template <int D, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int H, int H_kv, int N, int BH, float scale,
-    float softcap) {
+    float softcap, int wl, int wr) {
   constexpr int KC = D / 16;  // 16-wide k chunks over d
   constexpr int NT = D / 32;  // 32-wide column tiles over d
   // Double buffers as separate variables: the compiler gives each LDS
@@ -120,12 +122,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
   const float zs = scale * kLog2e;
   const float lse_mul = SOFTCAP ? kLog2e : -1.f / scale;
-  const int n_qblk = (N + BR - 1) / BR;
-  const int i_first = CAUSAL ? (k0 / BR) : 0;
-  const int n_iter = (n_qblk - i_first) * G;
+  // Query blocks [i_lo, i_hi) hold every row that sees a key of this block.
+  const int k_end = min(k0 + BC, N);
+  const int i_lo = max(0, k0 - wr) / BR;
+  const int i_hi = (min(N, k_end + wl) + BR - 1) / BR;
+  const int n_iter = (i_hi - i_lo) * G;
   const bool ragged_keys = k0 + BC > N;
-  const int q_last = (n_qblk - 1) * BR;  // first row of the last (possibly ragged) query block
-  const int rows_last = N - q_last;      // its valid rows
+  const int q_last = (i_hi - 1) * BR;  // first row of the last query block visited
 
   // Tiles run over the query heads of the group and, within a head, over the
   // query blocks from the last one down (concurrent workgroups of a head sweep
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // divisions; one cursor feeds the copies, one the compute.
   const int64_t head0 = (int64_t(b) * H + hk * G) * N;
   auto advance = [&](Cursor& c) {
-    if (c.q0 == i_first * BR) {
+    if (c.q0 == i_lo * BR) {
       c.q0 = q_last;
       c.row0 += N;
     } else {
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qg = q0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool ok = CAUSAL ? (qg >= my_key && qg < N) : (qg < N && my_key < N);
+        const bool ok = qg < N && my_key < N && my_key <= qg + wr && my_key >= qg - wl;
         a[r] = ok ? a[r] : fill;
       }
     };
@@ -408,7 +411,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   }
   advance(ci);
   auto tile = [&](auto bufc, int t) {
-    const bool masked = (CAUSAL && cc.q0 < k0 + BC) || ragged_keys || cc.q0 + BR > N;
+    // Unmasked: every key of the block is visible to every row of the tile.
+    const bool masked = ragged_keys || cc.q0 + BR > N || k0 < cc.q0 + BR - 1 - wl || k0 + BC - 1 > cc.q0 + wr;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // tile t in this buffer; the other buffer no longer read
     // After the last tile the copy repeats the current tile into the idle
@@ -438,26 +442,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   }
 }
 
-template <int D, bool CAUSAL, bool SOFTCAP>
+template <int D, bool SOFTCAP>
 hipError_t dkdv_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                   const float* Dv, void* dK, void* dV, hipStream_t s) {
   const int BH = p.B * p.H_kv;
   const int n_kblk = (p.N + BC - 1) / BC;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SOFTCAP>), dim3(unsigned(BH) * unsigned(n_kblk)), dim3(kThreads),
-                     0, s, static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K),
-                     static_cast<const bf16_t*>(V), static_cast<const bf16_t*>(dO), LSE, Dv,
-                     static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV), p.H, p.H_kv, p.N, BH, p.scale, p.softcap);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, SOFTCAP>), dim3(unsigned(BH) * unsigned(n_kblk)), dim3(kThreads), 0, s,
+                     static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V),
+                     static_cast<const bf16_t*>(dO), LSE, Dv, static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV), p.H,
+                     p.H_kv, p.N, BH, p.scale, p.softcap, p.wl, p.wr);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t dkdv_d(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                   const float* Dv, void* dK, void* dV, hipStream_t s) {
-  const bool sc = p.softcap > 0.f;
-  if (p.causal) return sc ? dkdv_t<D, true, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, s)
-                          : dkdv_t<D, true, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, s);
-  return sc ? dkdv_t<D, false, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, s)
-            : dkdv_t<D, false, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, s);
+  return p.softcap > 0.f ? dkdv_t<D, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, s)
+                         : dkdv_t<D, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, s);
 }
 
 }  // namespace

@@ -33,11 +33,13 @@ constexpr int kThreads = 256;
 constexpr int BQ = 128;  // query rows per workgroup
 constexpr int BK = 64;   // keys per inner step
 
-template <int D, bool CAUSAL, bool SOFTCAP>
+// Key k is visible to query q iff q - wl <= k <= q + wr and k < N (causal:
+// wr = 0; an unbounded side is N).
+template <int D, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    float* __restrict__ dQacc, int H, int H_kv, int N, int BHq, float scale, float softcap) {
+    float* __restrict__ dQacc, int H, int H_kv, int N, int BHq, float scale, float softcap, int wl, int wr) {
   constexpr int KC = D / 16;
   constexpr int NT = D / 32;
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BK * D];
@@ -76,8 +78,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int n = 0; n < NT; ++n) dq_acc[n] = f32x16_t{};
 
-  const int kv_end = CAUSAL ? min(N, q0 + BQ) : N;
-  const int n_steps = (kv_end + BK - 1) / BK;
+  // Key blocks [s_lo, s_hi) hold every key that some row of this block sees.
+  const int q_hi = min(q0 + BQ, N) - 1;  // last valid row
+  const int s_lo = max(0, q0 - wl) / BK;
+  const int s_hi = (min(N, q_hi + wr + 1) + BK - 1) / BK;
 
   // Per-lane byte offsets of the K/V block copies: slab I = s*4 + w covers
   // rows I*RPS ..; lane L fills physical chunk L % (D/8) of row I*RPS + L/(D/8),
@@ -112,14 +116,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  issue(0);
-  for (int step = 0; step < n_steps; ++step) {
+  if (s_lo < s_hi) issue(s_lo);
+  for (int step = s_lo; step < s_hi; ++step) {
     const int buf = step & 1;
     const int kb = step * BK;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // block `step` in LDS; buffer (step+1)%2 no longer read
-    if (step + 1 < n_steps) issue(step + 1);
-    const bool masked = (CAUSAL && kb + BK > q0) || kb + BK > N;
+    if (step + 1 < s_hi) issue(step + 1);
+    // Unmasked: every key of the block is visible to every row of this block.
+    const bool masked = kb + BK > N || kb < q_hi - wl || kb + BK - 1 > q0 + wr;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       // S^T, dP^T for keys kb + 32 s .. + 31 (rows) x this wave's 32 queries (columns).
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         float p = fast_exp2(fmaf(x, zs, nl2));
         if (masked) {
           const int key = kb + 32 * s + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= N || (CAUSAL && key > my_q)) p = 0.f;
+          if (key >= N || key > my_q + wr || key < my_q - wl) p = 0.f;
         }
         float ds = p * (dpt[r] - dval);
         if (SOFTCAP) ds *= dt;
@@ -180,26 +185,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-template <int D, bool CAUSAL, bool SOFTCAP>
+template <int D, bool SOFTCAP>
 hipError_t dq_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                 const float* Dv, float* dQacc, hipStream_t s) {
   const int BHq = p.B * p.H;
   const int n_qblk = (p.N + BQ - 1) / BQ;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, SOFTCAP>), dim3(unsigned(BHq) * unsigned(n_qblk)), dim3(kThreads),
-                     0, s, static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K),
-                     static_cast<const bf16_t*>(V), static_cast<const bf16_t*>(dO), LSE, Dv, dQacc, p.H, p.H_kv,
-                     p.N, BHq, p.scale, p.softcap);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, SOFTCAP>), dim3(unsigned(BHq) * unsigned(n_qblk)), dim3(kThreads), 0, s,
+                     static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V),
+                     static_cast<const bf16_t*>(dO), LSE, Dv, dQacc, p.H, p.H_kv, p.N, BHq, p.scale, p.softcap,
+                     p.wl, p.wr);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t dq_d(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                 const float* Dv, float* dQacc, hipStream_t s) {
-  const bool sc = p.softcap > 0.f;
-  if (p.causal) return sc ? dq_t<D, true, true>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
-                          : dq_t<D, true, false>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
-  return sc ? dq_t<D, false, true>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
-            : dq_t<D, false, false>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
+  return p.softcap > 0.f ? dq_t<D, true>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
+                         : dq_t<D, false>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
 }
 
 }  // namespace

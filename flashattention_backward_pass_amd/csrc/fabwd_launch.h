@@ -15,6 +15,9 @@ struct Problem {
   float scale;
   float softcap;
   bool deterministic = false;  // fp32: no atomics (query-block-outer dQ kernel)
+  // Visible band: key k is visible to query q iff q - wl <= k <= q + wr (and
+  // k < N).  Causal gives wr = 0; an unbounded side is N.
+  int wl = 0, wr = 0;
   int group() const { return H / H_kv; }
   int64_t q_rows() const { return int64_t(B) * H * N; }
   int64_t q_elems() const { return q_rows() * d; }

@@ -33,10 +33,13 @@ constexpr int BK = 64;   // keys per LDS block
 constexpr float kLazy = 8.f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int D, bool CAUSAL, bool SOFTCAP>
+// Key k is visible to query q iff q - wl <= k <= q + wr and k < N (causal:
+// wr = 0; an unbounded side is N).
+template <int D, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    bf16_t* __restrict__ O, float* __restrict__ LSE, int H, int H_kv, int N, int BHq, float scale, float softcap) {
+    bf16_t* __restrict__ O, float* __restrict__ LSE, int H, int H_kv, int N, int BHq, float scale, float softcap,
+    int wl, int wr) {
   constexpr int KC = D / 16;
   constexpr int NT = D / 32;
   // Double buffers as separate variables (own alias scopes: reads of one
@@ -76,8 +79,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   float m = -__builtin_inff();  // running max of S' tau log2e for this query
   float l = 0.f;                // this lane's share of the row sum (its keys)
 
-  const int kv_end = CAUSAL ? min(N, q0 + BQ) : N;
-  const int n_steps = (kv_end + BK - 1) / BK;
+  // Key blocks seen by some row of this block: [s_lo, s_hi).  Blocks in
+  // [p_lo, p_hi) are visible to every row (no mask); the others are partly
+  // masked (left window edge, diagonal / right edge, ragged end).
+  const int q_hi = min(q0 + BQ, N) - 1;  // last valid row
+  const int s_lo = max(0, q0 - wl) / BK;
+  const int s_hi = (min(N, q_hi + wr + 1) + BK - 1) / BK;
+  const int p_lo = min(s_hi, max(s_lo, (max(0, q_hi - wl) + BK - 1) / BK));
+  const int p_hi = max(p_lo, min(s_hi, min((q0 + wr + 1) / BK, N / BK)));
+  const int n_steps = s_hi - s_lo;
+  // Position -> key block: the unmasked blocks first, then the masked ones.
+  auto block_at = [&](int pos) {
+    const int n_plain = p_hi - p_lo, n_pre = p_lo - s_lo;
+    if (pos < n_plain) return p_lo + pos;
+    if (pos < n_plain + n_pre) return s_lo + (pos - n_plain);
+    return p_hi + (pos - n_plain - n_pre);
+  };
 
   // K/V block copies (buffer loads that write LDS); descriptors span the
   // block's valid rows, reads past N return zeros and the tiles start zeroed.
@@ -89,8 +106,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int row = (s * 4 + w) * RPS + lane / (D / 8);
     voff[s] = (row * D + 8 * ((lane % (D / 8)) ^ swz<D>(row))) * 2;
   }
-  auto issue = [&](auto bufc, int step) {
-    const int kb = step * BK;
+  auto issue = [&](auto bufc, int blk) {
+    const int kb = blk * BK;
     const int rows = min(BK, N - kb);
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(K + (kv_off + kb) * D), 0, rows * D * 2, 0x00020000);
@@ -130,7 +147,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kb + 32 * s + 8 * (r >> 2) + 4 * g + (r & 3);
-        st[r] = (key < N && (!CAUSAL || key <= my_q)) ? 0.f : -__builtin_inff();
+        st[r] = (key < N && key <= my_q + wr && key >= my_q - wl) ? 0.f : -__builtin_inff();
       }
     }
 #pragma unroll
@@ -202,30 +219,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  auto step_fn = [&](auto bufc, auto maskc, int step) __attribute__((always_inline)) {
+  auto step_fn = [&](auto bufc, auto maskc, int pos) __attribute__((always_inline)) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // block `step` in this buffer; the other buffer no longer read
-    if (step + 1 < n_steps) issue(std::integral_constant<int, 1 - decltype(bufc)::value>{}, step + 1);
-    half(bufc, maskc, step * BK, 0);
-    half(bufc, maskc, step * BK, 1);
+    __syncthreads();  // block at `pos` in this buffer; the other buffer no longer read
+    if (pos + 1 < n_steps) issue(std::integral_constant<int, 1 - decltype(bufc)::value>{}, block_at(pos + 1));
+    const int kb = block_at(pos) * BK;
+    half(bufc, maskc, kb, 0);
+    half(bufc, maskc, kb, 1);
   };
-  issue(B0{}, 0);
-  // Blocks that need a mask (causal diagonal, ragged end) are a suffix.
-  const int n_plain = min(n_steps, (CAUSAL ? min(q0, N) : N) / BK);
-  int step = 0;
-  for (; step + 2 <= n_plain; step += 2) {
-    step_fn(B0{}, std::false_type{}, step);
-    step_fn(B1{}, std::false_type{}, step + 1);
+  if (n_steps > 0) issue(B0{}, block_at(0));
+  const int n_plain = p_hi - p_lo;
+  int pos = 0;
+  for (; pos + 2 <= n_plain; pos += 2) {
+    step_fn(B0{}, std::false_type{}, pos);
+    step_fn(B1{}, std::false_type{}, pos + 1);
   }
-  if (step < n_plain) {
-    step_fn(B0{}, std::false_type{}, step);
-    ++step;
+  if (pos < n_plain) {
+    step_fn(B0{}, std::false_type{}, pos);
+    ++pos;
   }
-  for (; step < n_steps; ++step) {
-    if (step & 1)
-      step_fn(B1{}, std::true_type{}, step);
+  for (; pos < n_steps; ++pos) {
+    if (pos & 1)
+      step_fn(B1{}, std::true_type{}, pos);
     else
-      step_fn(B0{}, std::true_type{}, step);
+      step_fn(B0{}, std::true_type{}, pos);
   }
 
   // Epilogue: l over both key groups; O = O^T / l (4 consecutive d per
@@ -246,22 +263,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-template <int D, bool CAUSAL, bool SOFTCAP>
+template <int D, bool SOFTCAP>
 hipError_t fwd_t(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE, hipStream_t s) {
   const int BHq = p.B * p.H;
   const int n_qblk = (p.N + BQ - 1) / BQ;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, CAUSAL, SOFTCAP>), dim3(unsigned(BHq) * unsigned(n_qblk)), dim3(kThreads),
-                     0, s, static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K),
-                     static_cast<const bf16_t*>(V), static_cast<bf16_t*>(O), LSE, p.H, p.H_kv, p.N, BHq, p.scale,
-                     p.softcap);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, SOFTCAP>), dim3(unsigned(BHq) * unsigned(n_qblk)), dim3(kThreads), 0, s,
+                     static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V),
+                     static_cast<bf16_t*>(O), LSE, p.H, p.H_kv, p.N, BHq, p.scale, p.softcap, p.wl, p.wr);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t fwd_d(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE, hipStream_t s) {
-  const bool sc = p.softcap > 0.f;
-  if (p.causal) return sc ? fwd_t<D, true, true>(p, Q, K, V, O, LSE, s) : fwd_t<D, true, false>(p, Q, K, V, O, LSE, s);
-  return sc ? fwd_t<D, false, true>(p, Q, K, V, O, LSE, s) : fwd_t<D, false, false>(p, Q, K, V, O, LSE, s);
+  return p.softcap > 0.f ? fwd_t<D, true>(p, Q, K, V, O, LSE, s) : fwd_t<D, false>(p, Q, K, V, O, LSE, s);
 }
 
 }  // namespace

@@ -24,11 +24,13 @@ constexpr int kThreads = 256;
 
 // ----------------------------------------------------------------- forward
 // One workgroup per (query block of 32 rows, head, batch); 8 lanes per row.
-template <typename T, int D, bool CAUSAL, bool SOFTCAP>
+// Key k is visible to query q iff q - wl <= k <= q + wr and k < N (causal:
+// wr = 0; an unbounded side is N).
+template <typename T, int D, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                               const T* __restrict__ V, T* __restrict__ O,
                                                               float* __restrict__ LSE, int H, int H_kv, int N,
-                                                              float scale, float softcap) {
+                                                              float scale, float softcap, int wl, int wr) {
   constexpr int BQ = 32, BK = 64, DX = D / 8;
   __shared__ float sQ[BQ][D];
   __shared__ float sK[BK][D + 1];
@@ -52,9 +54,11 @@ __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(const T* __restric
 #pragma unroll
   for (int k = 0; k < DX; ++k) acc[k] = 0.f;
 
-  const int kv_end = CAUSAL ? min(N, q0 + BQ) : N;
+  // Keys visible to some row of the block.
+  const int kv_begin = max(0, q0 - wl) / BK * BK;
+  const int kv_end = min(N, min(q0 + BQ, N) + wr);
   const float zscale = scale * kLog2e;
-  for (int k0 = 0; k0 < kv_end; k0 += BK) {
+  for (int k0 = kv_begin; k0 < kv_end; k0 += BK) {
     __syncthreads();
     for (int idx = t; idx < BK * D; idx += kThreads) {
       const int kk = idx / D, x = idx % D;
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(const T* __restric
       for (int x = 0; x < D; ++x) s = fmaf(sQ[r][x], sK[c][x], s);
       if (SOFTCAP) s = softcap * tanh_f32(s / softcap);
       float zz = s * zscale;
-      if (key >= N || (CAUSAL && key > row)) zz = -INFINITY;
+      if (key >= N || key > row + wr || key < row - wl) zz = -INFINITY;
       z[m] = zz;
       bmax = fmaxf(bmax, zz);
     }
@@ -112,14 +116,14 @@ __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(const T* __restric
 // ----------------------------------------------------------------- backward
 // One workgroup per (key block of 32 keys, key/value head, batch); it loops
 // over the query heads of its group and over query blocks of 32 rows.
-template <typename T, int D, bool CAUSAL, bool SOFTCAP, bool ATOMIC_DQ>
+template <typename T, int D, bool SOFTCAP, bool ATOMIC_DQ>
 __global__ __launch_bounds__(kThreads) void bwd_simple_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                               const T* __restrict__ V, const T* __restrict__ dO,
                                                               const float* __restrict__ LSE,
                                                               const float* __restrict__ Dv,
                                                               float* __restrict__ dQacc, T* __restrict__ dK,
                                                               T* __restrict__ dV, int H, int H_kv, int N,
-                                                              float scale, float softcap) {
+                                                              float scale, float softcap, int wl, int wr) {
   constexpr int BK = 32, BQ = 32, DX = D / 8;
   __shared__ float sK[BK][D + 1];
   __shared__ float sV[BK][D + 1];
@@ -146,11 +150,13 @@ __global__ __launch_bounds__(kThreads) void bwd_simple_kernel(const T* __restric
   for (int k = 0; k < DX; ++k) acc_dk[k] = acc_dv[k] = 0.f;
 
   const float zscale = scale * kLog2e;
-  const int q_begin = CAUSAL ? (k0 / BQ) * BQ : 0;
+  // Query rows that see some key of the block.
+  const int q_begin = max(0, k0 - wr) / BQ * BQ;
+  const int q_end = min(N, min(k0 + BK, N) + wl);
   for (int hg = 0; hg < G; ++hg) {
     const int h = hk * G + hg;
     const int64_t q_off = (int64_t(b) * H + h) * N;
-    for (int q0 = q_begin; q0 < N; q0 += BQ) {
+    for (int q0 = q_begin; q0 < q_end; q0 += BQ) {
       __syncthreads();
       for (int idx = t; idx < BQ * D; idx += kThreads) {
         const int rr = idx / D, x = idx % D;
@@ -180,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void bwd_simple_kernel(const T* __restric
           s = softcap * th;
           dtanh = 1.f - th * th;
         }
-        const bool masked = key >= N || row >= N || (CAUSAL && key > row);
+        const bool masked = key >= N || row >= N || key > row + wr || key < row - wl;
         const float p = masked ? 0.f : fast_exp2(s * zscale - sL[r]);
         sP[r][c] = p;
         sdS[r][c] = p * (dp - sD[r]) * dtanh;
@@ -228,11 +234,11 @@ __global__ __launch_bounds__(kThreads) void bwd_simple_kernel(const T* __restric
 // its rows and keeps dQ in registers; every sum runs in a fixed order and
 // dQaccum is written once with plain stores, so the result is bitwise
 // reproducible.  8 lanes per row, lane `sub` owns columns sub + 8k.
-template <typename T, int D, bool CAUSAL, bool SOFTCAP>
+template <typename T, int D, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads) void bwd_dq_simple_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv, float* __restrict__ dQacc, int H, int H_kv, int N,
-    float scale, float softcap) {
+    float scale, float softcap, int wl, int wr) {
   constexpr int BQ = 32, BK = 32, DX = D / 8;
   __shared__ float sQ[BQ][D + 1];
   __shared__ float sdO[BQ][D + 1];
@@ -260,8 +266,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_simple_kernel(
 #pragma unroll
   for (int k = 0; k < DX; ++k) acc[k] = 0.f;
 
-  const int kv_end = CAUSAL ? min(N, q0 + BQ) : N;
-  for (int k0 = 0; k0 < kv_end; k0 += BK) {
+  const int kv_begin = max(0, q0 - wl) / BK * BK;
+  const int kv_end = min(N, min(q0 + BQ, N) + wr);
+  for (int k0 = kv_begin; k0 < kv_end; k0 += BK) {
     __syncthreads();
     for (int idx = t; idx < BK * D; idx += kThreads) {
       const int kk = idx / D, x = idx % D;
@@ -285,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_simple_kernel(
         s = softcap * th;
         dtanh = 1.f - th * th;
       }
-      const bool masked = key >= N || row >= N || (CAUSAL && key > row);
+      const bool masked = key >= N || row >= N || key > row + wr || key < row - wl;
       const float p = masked ? 0.f : fast_exp2(s * zscale - lse2);
       sdS[r][c] = p * (dp - dval) * dtanh;
     }
@@ -304,65 +311,56 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_simple_kernel(
   }
 }
 
-template <typename T, int D, bool C, bool S>
+template <typename T, int D, bool S>
 hipError_t fwd_simple_t(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,
                         hipStream_t s) {
   dim3 grid((p.N + 31) / 32, p.H, p.B);
-  hipLaunchKernelGGL((fwd_simple_kernel<T, D, C, S>), grid, dim3(kThreads), 0, s, static_cast<const T*>(Q),
+  hipLaunchKernelGGL((fwd_simple_kernel<T, D, S>), grid, dim3(kThreads), 0, s, static_cast<const T*>(Q),
                      static_cast<const T*>(K), static_cast<const T*>(V), static_cast<T*>(O), LSE, p.H, p.H_kv,
-                     p.N, p.scale, p.softcap);
+                     p.N, p.scale, p.softcap, p.wl, p.wr);
   return hipGetLastError();
 }
 
-template <typename T, int D, bool C, bool S>
+template <typename T, int D, bool S>
 hipError_t bwd_simple_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                         const float* LSE, const float* Dv, float* dQacc, void* dK, void* dV, hipStream_t s) {
   dim3 grid((p.N + 31) / 32, p.H_kv, p.B);
-  auto kern = p.deterministic ? bwd_simple_kernel<T, D, C, S, false> : bwd_simple_kernel<T, D, C, S, true>;
+  auto kern = p.deterministic ? bwd_simple_kernel<T, D, S, false> : bwd_simple_kernel<T, D, S, true>;
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, static_cast<const T*>(Q), static_cast<const T*>(K),
                      static_cast<const T*>(V), static_cast<const T*>(dO), LSE, Dv, dQacc, static_cast<T*>(dK),
-                     static_cast<T*>(dV), p.H, p.H_kv, p.N, p.scale, p.softcap);
+                     static_cast<T*>(dV), p.H, p.H_kv, p.N, p.scale, p.softcap, p.wl, p.wr);
   return hipGetLastError();
 }
 
-template <typename T, int D, bool C, bool S>
+template <typename T, int D, bool S>
 hipError_t bwd_dq_simple_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                            const float* LSE, const float* Dv, float* dQacc, hipStream_t s) {
   dim3 grid((p.N + 31) / 32, p.H, p.B);
-  hipLaunchKernelGGL((bwd_dq_simple_kernel<T, D, C, S>), grid, dim3(kThreads), 0, s, static_cast<const T*>(Q),
+  hipLaunchKernelGGL((bwd_dq_simple_kernel<T, D, S>), grid, dim3(kThreads), 0, s, static_cast<const T*>(Q),
                      static_cast<const T*>(K), static_cast<const T*>(V), static_cast<const T*>(dO), LSE, Dv,
-                     dQacc, p.H, p.H_kv, p.N, p.scale, p.softcap);
+                     dQacc, p.H, p.H_kv, p.N, p.scale, p.softcap, p.wl, p.wr);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t fwd_simple_d(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,
                         hipStream_t s) {
-  const bool sc = p.softcap > 0.f;
-  if (p.causal) return sc ? fwd_simple_t<T, D, true, true>(p, Q, K, V, O, LSE, s)
-                          : fwd_simple_t<T, D, true, false>(p, Q, K, V, O, LSE, s);
-  return sc ? fwd_simple_t<T, D, false, true>(p, Q, K, V, O, LSE, s)
-            : fwd_simple_t<T, D, false, false>(p, Q, K, V, O, LSE, s);
+  return p.softcap > 0.f ? fwd_simple_t<T, D, true>(p, Q, K, V, O, LSE, s)
+                         : fwd_simple_t<T, D, false>(p, Q, K, V, O, LSE, s);
 }
 
 template <typename T, int D>
 hipError_t bwd_simple_d(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                         const float* LSE, const float* Dv, float* dQacc, void* dK, void* dV, hipStream_t s) {
-  const bool sc = p.softcap > 0.f;
-  if (p.causal) return sc ? bwd_simple_t<T, D, true, true>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s)
-                          : bwd_simple_t<T, D, true, false>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s);
-  return sc ? bwd_simple_t<T, D, false, true>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s)
-            : bwd_simple_t<T, D, false, false>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s);
+  return p.softcap > 0.f ? bwd_simple_t<T, D, true>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s)
+                         : bwd_simple_t<T, D, false>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s);
 }
 
 template <typename T, int D>
 hipError_t bwd_dq_simple_d(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                            const float* LSE, const float* Dv, float* dQacc, hipStream_t s) {
-  const bool sc = p.softcap > 0.f;
-  if (p.causal) return sc ? bwd_dq_simple_t<T, D, true, true>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
-                          : bwd_dq_simple_t<T, D, true, false>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
-  return sc ? bwd_dq_simple_t<T, D, false, true>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
-            : bwd_dq_simple_t<T, D, false, false>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
+  return p.softcap > 0.f ? bwd_dq_simple_t<T, D, true>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
+                         : bwd_dq_simple_t<T, D, false>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
 }
 
 }  // namespace

@@ -33,6 +33,7 @@ class Workload:
     tau: float          # softmax scale
     sigma_qk: float     # standard deviation of Q and K entries (V and dO: 1)
     seed: int
+    window: tuple = (-1, -1)  # local mask (window_left, window_right); -1 = unbounded side
 
     @property
     def torch_dtype(self):
@@ -42,8 +43,25 @@ class Workload:
     def group(self) -> int:
         return self.H // self.H_kv
 
+    def visible_pairs(self) -> int:
+        """Number of (query, key) pairs of one head that the masks leave visible."""
+        import numpy as np
+        n = self.N
+        i = np.arange(n, dtype=np.int64)
+        wl, wr = self.window
+        lo = np.maximum(0, i - wl) if wl >= 0 else np.zeros(n, dtype=np.int64)
+        hi = np.full(n, n - 1, dtype=np.int64)
+        if wr >= 0:
+            hi = np.minimum(hi, i + wr)
+        if self.causal:
+            hi = np.minimum(hi, i)
+        return int(np.maximum(hi - lo + 1, 0).sum())
+
     def flops(self) -> float:
-        """Backward FLOPs of the metric: 10 N^2 d per query head, halved when causal."""
+        """Backward FLOPs of the metric: 10 N^2 d per query head, halved when causal.
+        With a local window: 10 d per visible (query, key) pair."""
+        if tuple(self.window) != (-1, -1):
+            return 10.0 * self.B * self.H * self.d * self.visible_pairs()
         f = 10.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2.0 if self.causal else f
 
@@ -51,11 +69,11 @@ class Workload:
         return asdict(self)
 
 
-def _wl(name, B, H, H_kv, N, d, dtype, causal, softcap, sigma_qk, seed):
-    return Workload(name, B, H, H_kv, N, d, dtype, causal, softcap, 1.0 / math.sqrt(d), sigma_qk, seed)
+def _wl(name, B, H, H_kv, N, d, dtype, causal, softcap, sigma_qk, seed, window=(-1, -1)):
+    return Workload(name, B, H, H_kv, N, d, dtype, causal, softcap, 1.0 / math.sqrt(d), sigma_qk, seed, window)
 
 
-# The five workloads of the parity and performance suite.
+# The workloads of the parity and performance suite.
 WORKLOADS = {
     w.name: w
     for w in [
@@ -64,16 +82,20 @@ WORKLOADS = {
         _wl("bf16_softcap30_b4h16_n2048_d128", 4, 16, 16, 2048, 128, "bf16", False, 30.0, 1.5, 1002),
         _wl("bf16_gqa32x8_causal_b1_n4096_d128", 1, 32, 8, 4096, 128, "bf16", True, 0.0, 1.0, 1003),
         _wl("bf16_causal_b1h8_n16384_d128", 1, 8, 8, 16384, 128, "bf16", True, 0.0, 1.0, 1004),
+        # Local (sliding-window) variant of the long workload: each query sees
+        # itself and the 2048 keys before it.
+        _wl("bf16_local2048_causal_b1h8_n16384_d128", 1, 8, 8, 16384, 128, "bf16", True, 0.0, 1.0, 1005,
+            (2048, -1)),
     ]
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
 
 def custom(B, H, H_kv, N, d, dtype="bf16", causal=False, softcap=0.0, tau=None, sigma_qk=1.0, seed=0,
-           name="custom") -> Workload:
+           name="custom", window=(-1, -1)) -> Workload:
     """A workload of any shape, for edge-case tests (ragged N, tiny sizes, ...)."""
     return Workload(name, B, H, H_kv, N, d, dtype, causal, float(softcap),
-                    float(tau) if tau is not None else 1.0 / math.sqrt(d), sigma_qk, seed)
+                    float(tau) if tau is not None else 1.0 / math.sqrt(d), sigma_qk, seed, tuple(window))
 
 
 def make_inputs(w: Workload):

@@ -30,6 +30,11 @@
  *    Z = scale * c * tanh(R / c), otherwise Z = scale * R ([CB] 2.1: the cap
  *    acts on the raw scores; the softmax scale multiplies the capped value).
  *    Causal: key j is masked for query i when j > i (the diagonal is kept).
+ *    Local window ([CB] 3.4 names a masking phase for a local window's
+ *    boundary; the band below is this library's reading): with
+ *    window_left >= 0, key j is masked for query i when j < i - window_left;
+ *    with window_right >= 0, when j > i + window_right.  Both combine with
+ *    the causal mask; -1 leaves a side unbounded, so (-1, -1) is no window.
  *  - Every pointer must be 16-byte aligned.  Sizes with B*H*N*d beyond
  *    2^40 elements are rejected.  N = 0 or B = 0 is a valid empty problem:
  *    the call validates its arguments and enqueues nothing.
@@ -47,7 +52,7 @@ extern "C" {
 
 enum attn_status {
   ATTN_OK = 0,
-  ATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, H % H_kv != 0, scale <= 0, softcap < 0, ... */
+  ATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, H % H_kv != 0, scale <= 0, softcap < 0, window < -1, ... */
   ATTN_ERR_UNSUPPORTED = 2, /* no kernel instance for this (dtype, d) */
   ATTN_ERR_MISALIGNED = 3,  /* a pointer is not 16-byte aligned */
   ATTN_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
@@ -62,6 +67,8 @@ typedef struct attn_params {
   float scale;              /* softmax scale tau, finite and > 0 (usually 1/sqrt(d)) */
   float softcap;            /* c > 0 enables the tanh cap, 0 disables it */
   int32_t deterministic;    /* 0 or 1; see attn_bwd */
+  int32_t window_left;      /* local mask: key j hidden from query i when j < i - window_left; -1 = off */
+  int32_t window_right;     /* local mask: key j hidden from query i when j > i + window_right; -1 = off */
 } attn_params;
 
 /* Supported head dimensions: d = 64 and d = 128, for both dtypes. */

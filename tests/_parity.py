@@ -30,7 +30,7 @@ def run_gpu(w, x, *, o=None, lse=None, poison=False, deterministic=False):
     dev = torch.device("cuda:0")
     q, k, v, do = (x[n].to(dev) for n in ("Q", "K", "V", "dO"))
     if o is None:
-        o, lse = fab.attention_forward(q, k, v, causal=w.causal, scale=w.tau, softcap=w.softcap)
+        o, lse = fab.attention_forward(q, k, v, causal=w.causal, scale=w.tau, softcap=w.softcap, window=w.window)
     else:
         o, lse = o.to(dev), lse.to(dev)
     B, H, N, d = q.shape
@@ -40,9 +40,10 @@ def run_gpu(w, x, *, o=None, lse=None, poison=False, deterministic=False):
     if poison:
         for t in (D, acc, dq, dk, dv):
             t.fill_(float("nan"))
-    fab.attn_bwd_preprocess(o, do, D, acc, H_kv=w.H_kv, causal=w.causal, scale=w.tau, softcap=w.softcap)
+    fab.attn_bwd_preprocess(o, do, D, acc, H_kv=w.H_kv, causal=w.causal, scale=w.tau, softcap=w.softcap,
+                            window=w.window)
     fab.attn_bwd(q, k, v, do, lse, D, acc, dk, dv, causal=w.causal, scale=w.tau, softcap=w.softcap,
-                 deterministic=deterministic)
+                 deterministic=deterministic, window=w.window)
     acc_copy = acc.clone()
     fab.attn_bwd_dq_convert(acc, dq, scale=w.tau)
     torch.cuda.synchronize()
@@ -50,7 +51,7 @@ def run_gpu(w, x, *, o=None, lse=None, poison=False, deterministic=False):
 
 
 def oracle_full(w, x):
-    return oracle.reference(x["Q"], x["K"], x["V"], x["dO"], w.tau, w.causal, w.softcap)
+    return oracle.reference(x["Q"], x["K"], x["V"], x["dO"], w.tau, w.causal, w.softcap, w.window)
 
 
 def oracle_kv_heads(w, x, b, kv_heads):
@@ -62,8 +63,8 @@ def oracle_kv_heads(w, x, b, kv_heads):
         dk = dv = 0.0
         for h in range(g * G, (g + 1) * G):
             q, do = x["Q"][b, h], x["dO"][b, h]
-            O, L = oracle.forward_head(q, k, v, w.tau, w.causal, w.softcap)
-            dq, dk_h, dv_h, D = oracle.backward_head(q, k, v, O, do, L, w.tau, w.causal, w.softcap)
+            O, L = oracle.forward_head(q, k, v, w.tau, w.causal, w.softcap, w.window)
+            dq, dk_h, dv_h, D = oracle.backward_head(q, k, v, O, do, L, w.tau, w.causal, w.softcap, w.window)
             out["O"][h], out["LSE"][h], out["D"][h], out["dQ"][h] = O, L, D, dq
             dk = dk + dk_h
             dv = dv + dv_h

@@ -52,8 +52,16 @@ def test_status_strings(lib):
 
 
 def test_params_layout_matches_header():
-    # 7 int32 + 2 float + 1 int32, no padding
-    assert ctypes.sizeof(fab.attn_params) == 40
+    """The ctypes struct lists the header's fields, in order, with the same types."""
+    import re
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct attn_params {"):text.index("} attn_params;")]
+    fields = []
+    for typ, names in re.findall(r"^\s*(int32_t|float)\s+([^;]+);", body, re.M):
+        for n in names.split(","):
+            fields.append((n.strip(), ctypes.c_int32 if typ == "int32_t" else ctypes.c_float))
+    assert [(n, t) for n, t in fab.attn_params._fields_] == fields
+    assert ctypes.sizeof(fab.attn_params) == 4 * len(fields)  # no padding
 
 
 # Fake, 16-byte aligned, non-null device pointers: validation rejects the call
@@ -77,15 +85,16 @@ BAD = [
     dict(H=0), dict(H_kv=0), dict(H=6, H_kv=4), dict(N=-1), dict(B=-2), dict(d=0), dict(dtype=2),
     dict(causal=2), dict(scale=0.0), dict(scale=-1.0), dict(scale=float("nan")), dict(scale=float("inf")),
     dict(softcap=-1.0), dict(softcap=float("inf")), dict(N=(1 << 24) + 1),
+    dict(window_left=-2), dict(window_right=-3),
 ]
 
 
 @pytest.mark.parametrize("bad", BAD, ids=[str(b) for b in BAD])
 def test_invalid_arguments(lib, bad):
-    kw = dict(B=1, H=4, H_kv=2, N=64, d=64, dtype=1, causal=0, scale=0.125, softcap=0.0)
+    kw = dict(B=1, H=4, H_kv=2, N=64, d=64, dtype=1, causal=0, scale=0.125, softcap=0.0, deterministic=0,
+              window_left=-1, window_right=-1)
     kw.update(bad)
-    p = fab.attn_params(kw["B"], kw["H"], kw["H_kv"], kw["N"], kw["d"], kw["dtype"], kw["causal"], kw["scale"],
-                        kw["softcap"], 0)
+    p = fab.attn_params(**kw)
     assert call_all(lib, p) == [fab.ATTN_ERR_INVALID_ARG] * 4
 
 
@@ -137,3 +146,10 @@ def test_binding_fails_loudly_without_library(tmp_path):
             fab.load_library(str(tmp_path / "missing.so"))
     finally:
         fab._lib = saved
+
+
+@pytest.mark.parametrize("window", [(0, 0), (5, -1), (-1, 3), (1 << 24, 7)])
+def test_windows_accepted(lib, window):
+    # Valid windows on an empty problem: every argument is checked, nothing runs.
+    p = fab.make_params(1, 2, 2, 0, 64, 1, causal=1, window=window)
+    assert call_all(lib, p, ptr=None) == [fab.ATTN_OK] * 4
