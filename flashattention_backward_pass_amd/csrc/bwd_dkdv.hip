@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int H, int H_kv, int N, int BH, float scale,
-    float softcap, int wl, int wr) {
+    float softcap, int wl, int wr, int n_split, float* __restrict__ part) {
   constexpr int KC = D / 16;  // 16-wide k chunks over d
   constexpr int NT = D / 32;  // 32-wide column tiles over d
   // Double buffers as separate variables: the compiler gives each LDS
@@ -86,12 +86,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int l32 = lane & 31, g = lane >> 5;  // accumulator column / row group
   const int j16 = lane & 15, h16 = (lane >> 4) & 1;
 
-  // Work unit: (batch*kv-head, key block).  Key blocks vary slowest so that
-  // the heaviest causal blocks (small j) are dispatched first.
-  const int bh = blockIdx.x % BH;
-  const int jblk = blockIdx.x / BH;
+  // Work unit: (batch*kv-head, key block, head subset).  Key blocks vary
+  // slowest so that the heaviest causal blocks (small j) are dispatched first.
+  // With n_split > 1 the G query heads of the group are shared out over
+  // n_split workgroups, which write fp32 partial sums to `part`.
+  const int unit = blockIdx.x % (BH * n_split);
+  const int bh = unit % BH, split = unit / BH;
+  const int jblk = blockIdx.x / (BH * n_split);
   const int b = bh / H_kv, hk = bh % H_kv;
-  const int G = H / H_kv;
+  const int G = H / H_kv / n_split;  // query heads of this workgroup
   const int k0 = jblk * BC;
   const int64_t kv_off = (int64_t(b) * H_kv + hk) * N;  // row offset of this kv head
   const int kw = w * 32;                                 // this wave's first key in the block
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // query blocks from the last one down (concurrent workgroups of a head sweep
   // the same rows together).  A cursor steps through that sequence without
   // divisions; one cursor feeds the copies, one the compute.
-  const int64_t head0 = (int64_t(b) * H + hk * G) * N;
+  const int64_t head0 = (int64_t(b) * H + (hk * n_split + split) * G) * N;
   auto advance = [&](Cursor& c) {
     if (c.q0 == i_lo * BR) {
       c.q0 = q_last;
@@ -427,7 +430,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   }
 
   // Epilogue: dK = -tau * dK_acc (the accumulator holds -dS^T Q), dV = dV_acc
-  // (rows = keys, lanes = d).
+  // (rows = keys, lanes = d); with a head split, the raw fp32 accumulators
+  // go to `part` ([2][n_split][B*H_kv*N][D]: dK partials, then dV partials).
+  const int64_t plane = int64_t(BH) * N * D;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
 #pragma unroll
@@ -435,38 +440,90 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       const int key = k0 + kw + 8 * (r >> 2) + 4 * g + (r & 3);
       if (key < N) {
         const int64_t off = (kv_off + key) * D + 32 * n + l32;
-        dK[off].bits = f32_to_bf16(dk_acc[n][r] * -scale);
-        dV[off].bits = f32_to_bf16(dv_acc[n][r]);
+        if (n_split == 1) {
+          dK[off].bits = f32_to_bf16(dk_acc[n][r] * -scale);
+          dV[off].bits = f32_to_bf16(dv_acc[n][r]);
+        } else {
+          part[split * plane + off] = dk_acc[n][r];
+          part[(n_split + split) * plane + off] = dv_acc[n][r];
+        }
       }
     }
   }
 }
 
+// Sums the head-split partials in a fixed order and rounds: dK = -tau * sum,
+// dV = sum (8 elements per thread; `elems` = B*H_kv*N*D is a multiple of 8).
+__global__ __launch_bounds__(256) void dkdv_split_sum_kernel(const float* __restrict__ part, int n_split,
+                                                             int64_t elems, bf16_t* __restrict__ dK,
+                                                             bf16_t* __restrict__ dV, float scale) {
+  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (i >= elems) return;
+  float k[8], v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) k[e] = v[e] = 0.f;
+  for (int sp = 0; sp < n_split; ++sp) {
+    const f32x4_t* pk = reinterpret_cast<const f32x4_t*>(part + sp * elems + i);
+    const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(part + (n_split + sp) * elems + i);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4_t a = pk[h], c = pv[h];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k[4 * h + e] += a[e];
+        v[4 * h + e] += c[e];
+      }
+    }
+  }
+  u32x4_t ko, vo;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ko[e] = pack_bf16x2(k[2 * e] * -scale, k[2 * e + 1] * -scale);
+    vo[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+  }
+  *reinterpret_cast<u32x4_t*>(dK + i) = ko;
+  *reinterpret_cast<u32x4_t*>(dV + i) = vo;
+}
+
 template <int D, bool SOFTCAP>
 hipError_t dkdv_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                  const float* Dv, void* dK, void* dV, hipStream_t s) {
+                  const float* Dv, void* dK, void* dV, float* scratch, hipStream_t s) {
   const int BH = p.B * p.H_kv;
   const int n_kblk = (p.N + BC - 1) / BC;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, SOFTCAP>), dim3(unsigned(BH) * unsigned(n_kblk)), dim3(kThreads), 0, s,
-                     static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V),
-                     static_cast<const bf16_t*>(dO), LSE, Dv, static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV), p.H,
-                     p.H_kv, p.N, BH, p.scale, p.softcap, p.wl, p.wr);
+  // Grouped-query heads with few work units: the heaviest (first causal)
+  // key blocks would run G times every query tile in one workgroup.  Share
+  // the heads out over two workgroups; their fp32 partials fit in `scratch`
+  // (B*H*N*d floats) because 2 splits x (dK, dV) x B*H_kv*N*d <= B*H*N*d
+  // when G >= 4.
+  const int G = p.H / p.H_kv;
+  const int n_split = (scratch != nullptr && G >= 4 && int64_t(BH) * n_kblk < 1024) ? 2 : 1;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, SOFTCAP>), dim3(unsigned(BH) * unsigned(n_kblk) * unsigned(n_split)),
+                     dim3(kThreads), 0, s, static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K),
+                     static_cast<const bf16_t*>(V), static_cast<const bf16_t*>(dO), LSE, Dv,
+                     static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV), p.H, p.H_kv, p.N, BH, p.scale, p.softcap,
+                     p.wl, p.wr, n_split, n_split > 1 ? scratch : nullptr);
+  if (n_split == 1) return hipGetLastError();
+  const int64_t elems = int64_t(BH) * p.N * D;
+  const unsigned blocks = unsigned((elems / 8 + 255) / 256);
+  hipLaunchKernelGGL(dkdv_split_sum_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(scratch),
+                     n_split, elems, static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV), p.scale);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t dkdv_d(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                  const float* Dv, void* dK, void* dV, hipStream_t s) {
-  return p.softcap > 0.f ? dkdv_t<D, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, s)
-                         : dkdv_t<D, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, s);
+                  const float* Dv, void* dK, void* dV, float* scratch, hipStream_t s) {
+  return p.softcap > 0.f ? dkdv_t<D, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s)
+                         : dkdv_t<D, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_dkdv_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
-                                const float* LSE, const float* Dv, void* dK, void* dV, hipStream_t s) {
-  return p.d == 64 ? dkdv_d<64>(p, Q, K, V, dO, LSE, Dv, dK, dV, s)
-                   : dkdv_d<128>(p, Q, K, V, dO, LSE, Dv, dK, dV, s);
+                                const float* LSE, const float* Dv, void* dK, void* dV, float* scratch,
+                                hipStream_t s) {
+  return p.d == 64 ? dkdv_d<64>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s)
+                   : dkdv_d<128>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s);
 }
 
 }  // namespace fabwd

@@ -42,8 +42,11 @@ hipError_t launch_bwd_dq_simple(const Problem& p, const void* Q, const void* K, 
                                 const float* LSE, const float* Dv, float* dQacc, hipStream_t s);
 // bf16 matrix-core backward: dK/dV kernel (key blocks outer) and dQ kernel
 // (query blocks outer); the dQ kernel overwrites dQaccum.
+// scratch: B*H*N*d floats the kernel may use for partial sums before the
+// dQ kernel overwrites them (dQaccum), or nullptr.
 hipError_t launch_bwd_dkdv_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
-                                const float* LSE, const float* D, void* dK, void* dV, hipStream_t s);
+                                const float* LSE, const float* Dv, void* dK, void* dV, float* scratch,
+                                hipStream_t s);
 hipError_t launch_bwd_dq_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                               const float* LSE, const float* D, float* dQacc, hipStream_t s);
 

@@ -108,7 +108,11 @@ int attn_bwd_preprocess(const attn_params* p, const void* O, const void* dO,
  *   bf16: dK/dV come from a key-block-outer kernel and dQaccum from a
  *         query-block-outer kernel that recomputes S and dP and keeps dQ in
  *         registers; every row of dQaccum is overwritten with plain stores,
- *         so the result is bitwise reproducible (no atomics).
+ *         so the result is bitwise reproducible (no atomics).  With grouped
+ *         query heads (H / H_kv >= 4) and few key blocks, the dK/dV kernel
+ *         shares each group's heads over two workgroups and keeps their fp32
+ *         partial sums in dQaccum until a fixed-order sum writes dK, dV; the
+ *         dQ kernel then overwrites dQaccum.
  *   fp32, deterministic = 0: one kernel adds the dQ partials of each key
  *         block into the zeroed dQaccum with fp32 atomics ([CB] 6.2); the
  *         order of those additions is not fixed, so the low bits of dQ may
