@@ -13,4 +13,6 @@ from .attention import (  # noqa: F401
     backward_q_rows_head,
     backward_kv_rows_head,
     reference,
+    head_dropout,
 )
+from . import philox  # noqa: F401

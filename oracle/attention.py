@@ -35,7 +35,13 @@ Readings taken where the pages are silent or ambiguous:
   * the local mask: the backward-kernel page names a third masking phase for
     the query blocks at a local window's boundary but gives no formula; the
     window is read as the band i - wl <= j <= i + wr around the diagonal,
-    combined with the causal mask when both are on.
+    combined with the causal mask when both are on;
+  * dropout: [FA1] section 3.3 and the dropout lines of Algorithm 4 apply the
+    replayed mask Z (elements 1/(1 - p) or 0) to P in the forward pass,
+    O = (P o Z) V, and give dV = (P o Z)^T dO (eq (10)) and dP = (dO V^T) o Z
+    (eq (12)); D = rowsum(dO o O) and dZ = P o (dP - D) are unchanged
+    (eqs (13), (14)).  The pages fix no generator: oracle/philox.py states the
+    Philox4x32-10 stream this build uses.  LSE stays that of the undropped P.
 
 Parity pins: tests/test_oracle_*.py (N=2, d=2 hand expansions of [FA1]
 section 2, central finite differences of <dO, O>, invariants, closed forms,
@@ -46,6 +52,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import philox
+
 __all__ = [
     "forward",
     "forward_head",
@@ -55,6 +63,7 @@ __all__ = [
     "backward_q_rows_head",
     "backward_kv_rows_head",
     "reference",
+    "head_dropout",
 ]
 
 
@@ -102,12 +111,13 @@ def _logits(q, k, q_idx, k_idx, tau, causal, softcap, window=None):
     return Z, T
 
 
-def forward_rows_head(q, k, v, rows, tau, causal=False, softcap=0.0, window=None):
+def forward_rows_head(q, k, v, rows, tau, causal=False, softcap=0.0, window=None, zdrop=None):
     """O and LSE of the query rows `rows` of one head, straight from the definition.
 
     q: [N, d], k, v: [N, d].  P_i = softmax(Z_i) ([FA1] 1.1), O_i = P_i V,
     LSE_i = m_i + ln sum_j exp(Z_ij - m_i) with m_i = max_j Z_ij, which equals
     [FA1] eq (9)'s pair (m, l) through LSE = m + ln l, as [CB] 1.2 stores it.
+    zdrop(rows, cols) -> dropout matrix Z, or None: O_i = (P_i o Z_i) V.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     rows = np.asarray(rows, dtype=np.int64)
@@ -117,16 +127,18 @@ def forward_rows_head(q, k, v, rows, tau, causal=False, softcap=0.0, window=None
     m = Z.max(axis=1)
     lse = m + np.log(np.exp(Z - m[:, None]).sum(axis=1))
     P = np.exp(Z - lse[:, None])
+    if zdrop is not None:
+        P = P * zdrop(rows, np.arange(k.shape[0]))
     return P @ v, lse
 
 
-def forward_head(q, k, v, tau, causal=False, softcap=0.0, window=None):
+def forward_head(q, k, v, tau, causal=False, softcap=0.0, window=None, zdrop=None):
     """O [N, d] and LSE [N] of one head (all rows)."""
     n = _f64(q).shape[0]
-    return forward_rows_head(q, k, v, np.arange(n), tau, causal, softcap, window)
+    return forward_rows_head(q, k, v, np.arange(n), tau, causal, softcap, window, zdrop)
 
 
-def backward_head(q, k, v, o, do, lse, tau, causal=False, softcap=0.0, window=None):
+def backward_head(q, k, v, o, do, lse, tau, causal=False, softcap=0.0, window=None, zdrop=None):
     """dQ, dK, dV [N, d] and D [N] of one head from the saved forward tensors.
 
     Inputs are what [CB] 1.3 says the forward saves (Q, K, V, O, LSE) plus dO.
@@ -137,6 +149,8 @@ def backward_head(q, k, v, o, do, lse, tau, causal=False, softcap=0.0, window=No
       dZ = P o (dP - D 1^T)             [FA1] eq (5)
       dR = tau dZ (1 - T^2) with cap, tau dZ without  ([CB] 2.1 (3); [FA1] 2.5)
       dQ = dR K,  dK = dR^T Q           [FA1] eqs (7), (8)
+    With dropout (zdrop(rows, cols) -> Z): dV = (P o Z)^T dO ([FA1] eq (10))
+    and dP = (dO V^T) o Z ([FA1] eq (12)).
     """
     q, k, v, o, do, lse = map(_f64, (q, k, v, o, do, lse))
     n = q.shape[0]
@@ -147,8 +161,11 @@ def backward_head(q, k, v, o, do, lse, tau, causal=False, softcap=0.0, window=No
     Z, T = _logits(q, k, idx, np.arange(k.shape[0]), tau, causal, softcap, window)
     P = np.exp(Z - lse[:, None])
     del Z
-    dV = P.T @ do
+    Zd = zdrop(idx, np.arange(k.shape[0])) if zdrop is not None else None
+    dV = (P * Zd).T @ do if Zd is not None else P.T @ do
     dP = do @ v.T
+    if Zd is not None:
+        dP = dP * Zd
     D = (do * o).sum(axis=1)
     dZ = P * (dP - D[:, None])
     del P, dP
@@ -162,7 +179,8 @@ def backward_head(q, k, v, o, do, lse, tau, causal=False, softcap=0.0, window=No
     return dQ, dK, dV, D
 
 
-def backward_q_rows_head(q, k, v, o_rows, do_rows, lse_rows, rows, tau, causal=False, softcap=0.0, window=None):
+def backward_q_rows_head(q, k, v, o_rows, do_rows, lse_rows, rows, tau, causal=False, softcap=0.0, window=None,
+                         zdrop=None):
     """dQ and D of the query rows `rows` of one head.
 
     Row i of dQ needs only row i of P, dP and D: dQ_i = sum_j dR_ij K_j
@@ -177,13 +195,15 @@ def backward_q_rows_head(q, k, v, o_rows, do_rows, lse_rows, rows, tau, causal=F
     Z, T = _logits(q[rows], k, rows, np.arange(k.shape[0]), tau, causal, softcap, window)
     P = np.exp(Z - lse_rows[:, None])
     dP = do_rows @ v.T
+    if zdrop is not None:
+        dP = dP * zdrop(rows, np.arange(k.shape[0]))
     D = (do_rows * o_rows).sum(axis=1)
     dZ = P * (dP - D[:, None])
     dR = tau * dZ * (1.0 - T * T) if T is not None else tau * dZ
     return dR @ k, D
 
 
-def backward_kv_rows_head(q, k, v, o, do, lse, kv_rows, tau, causal=False, softcap=0.0, window=None):
+def backward_kv_rows_head(q, k, v, o, do, lse, kv_rows, tau, causal=False, softcap=0.0, window=None, zdrop=None):
     """dK and dV of the key rows `kv_rows` contributed by one query head.
 
     Column j of P, dP and dZ over all query rows gives
@@ -197,10 +217,23 @@ def backward_kv_rows_head(q, k, v, o, do, lse, kv_rows, tau, causal=False, softc
     Zc, Tc = _logits(q, k[cols], np.arange(q.shape[0]), cols, tau, causal, softcap, window)
     Pc = np.exp(Zc - lse[:, None])
     dPc = do @ v[cols].T
+    Zd = zdrop(np.arange(q.shape[0]), cols) if zdrop is not None else None
+    if Zd is not None:
+        dPc = dPc * Zd
     D = (do * o).sum(axis=1)
     dZc = Pc * (dPc - D[:, None])
     dRc = tau * dZc * (1.0 - Tc * Tc) if Tc is not None else tau * dZc
-    return dRc.T @ q, Pc.T @ do
+    return dRc.T @ q, (Pc * Zd).T @ do if Zd is not None else Pc.T @ do
+
+
+def head_dropout(dropout, bh):
+    """zdrop(rows, cols) of query head bh (= b * H + h) for dropout = (p, seed, offset), or None.
+
+    p = 0 turns dropout off."""
+    if dropout is None or float(np.float32(dropout[0])) == 0.0:
+        return None
+    p, seed, offset = dropout
+    return lambda rows, cols: philox.dropout_multiplier(p, seed, offset, bh, rows, cols)
 
 
 def _group(H, H_kv):
@@ -209,10 +242,11 @@ def _group(H, H_kv):
     return H // H_kv
 
 
-def forward(Q, K, V, tau, causal=False, softcap=0.0, window=None):
+def forward(Q, K, V, tau, causal=False, softcap=0.0, window=None, dropout=None):
     """O [B,H,N,d] and LSE [B,H,N] for Q [B,H,N,d], K, V [B,H_kv,N,d].
 
     Query head h reads key/value head h // (H / H_kv) ([CB] 8.5).
+    dropout = (p, seed, offset) replays the mask of oracle/philox.py.
     """
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     B, H, N, d = Q.shape
@@ -221,11 +255,12 @@ def forward(Q, K, V, tau, causal=False, softcap=0.0, window=None):
     LSE = np.zeros((B, H, N))
     for b in range(B):
         for h in range(H):
-            O[b, h], LSE[b, h] = forward_head(Q[b, h], K[b, h // G], V[b, h // G], tau, causal, softcap, window)
+            O[b, h], LSE[b, h] = forward_head(Q[b, h], K[b, h // G], V[b, h // G], tau, causal, softcap, window,
+                                              head_dropout(dropout, b * H + h))
     return O, LSE
 
 
-def backward(Q, K, V, O, dO, LSE, tau, causal=False, softcap=0.0, window=None):
+def backward(Q, K, V, O, dO, LSE, tau, causal=False, softcap=0.0, window=None, dropout=None):
     """dQ [B,H,N,d], dK, dV [B,H_kv,N,d], D [B,H,N] from the saved tensors.
 
     dK and dV of key/value head g sum the contributions of its G query heads
@@ -242,7 +277,7 @@ def backward(Q, K, V, O, dO, LSE, tau, causal=False, softcap=0.0, window=None):
         for h in range(H):
             g = h // G
             dq, dk, dv, dd = backward_head(Q[b, h], K[b, g], V[b, g], O[b, h], dO[b, h], LSE[b, h],
-                                           tau, causal, softcap, window)
+                                           tau, causal, softcap, window, head_dropout(dropout, b * H + h))
             dQ[b, h] = dq
             dK[b, g] += dk
             dV[b, g] += dv
@@ -250,10 +285,11 @@ def backward(Q, K, V, O, dO, LSE, tau, causal=False, softcap=0.0, window=None):
     return dQ, dK, dV, D
 
 
-def reference(Q, K, V, dO, tau, causal=False, softcap=0.0, window=None):
+def reference(Q, K, V, dO, tau, causal=False, softcap=0.0, window=None, dropout=None):
     """Forward then backward in fp64: dict with O, LSE, D, dQ, dK, dV.
 
-    window = (wl, wr) adds the local mask (-1: that side unbounded)."""
-    O, LSE = forward(Q, K, V, tau, causal, softcap, window)
-    dQ, dK, dV, D = backward(Q, K, V, O, dO, LSE, tau, causal, softcap, window)
+    window = (wl, wr) adds the local mask (-1: that side unbounded);
+    dropout = (p, seed, offset) applies the replayed dropout mask."""
+    O, LSE = forward(Q, K, V, tau, causal, softcap, window, dropout)
+    dQ, dK, dV, D = backward(Q, K, V, O, dO, LSE, tau, causal, softcap, window, dropout)
     return {"O": O, "LSE": LSE, "D": D, "dQ": dQ, "dK": dK, "dV": dV}
