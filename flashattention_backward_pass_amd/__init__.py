@@ -50,6 +50,10 @@ class attn_params(ctypes.Structure):
         ("deterministic", ctypes.c_int32),
         ("window_left", ctypes.c_int32),
         ("window_right", ctypes.c_int32),
+        ("dropout_p", ctypes.c_float),
+        ("rng_seed_lo", ctypes.c_uint32),
+        ("rng_seed_hi", ctypes.c_uint32),
+        ("rng_offset", ctypes.c_uint32),
     ]
 
 
@@ -85,13 +89,19 @@ def status_str(status: int) -> str:
 
 
 def make_params(B, H, H_kv, N, d, dtype, causal=False, scale=None, softcap=0.0, deterministic=0,
-                window=None) -> attn_params:
-    """window = (window_left, window_right) local mask, -1 = unbounded side; None = no window."""
+                window=None, dropout=None) -> attn_params:
+    """window = (window_left, window_right) local mask, -1 = unbounded side; None = no window.
+    dropout = (p, seed, offset): dropout probability, 64-bit generator seed, 32-bit counter offset."""
     if scale is None:
         scale = d ** -0.5
     wl, wr = (-1, -1) if window is None else window
+    p_drop, seed, offset = (0.0, 0, 0) if dropout is None else dropout
+    seed = int(seed)
+    if not (0 <= seed < 1 << 64 and 0 <= int(offset) < 1 << 32):
+        raise ValueError("dropout seed must fit 64 bits and offset 32 bits")
     return attn_params(int(B), int(H), int(H_kv), int(N), int(d), int(dtype), int(bool(causal)),
-                       float(scale), float(softcap), int(deterministic), int(wl), int(wr))
+                       float(scale), float(softcap), int(deterministic), int(wl), int(wr), float(p_drop),
+                       seed & 0xFFFFFFFF, seed >> 32, int(offset))
 
 
 # ------------------------------------------------------------ torch marshalling
@@ -127,14 +137,14 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _params_from(q, k, causal, scale, softcap, deterministic=False, window=None) -> attn_params:
+def _params_from(q, k, causal, scale, softcap, deterministic=False, window=None, dropout=None) -> attn_params:
     B, H, N, d = q.shape
     if k.dim() != 4 or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
         raise ValueError(f"K shape {tuple(k.shape)} does not match Q shape {tuple(q.shape)}")
     if k.dtype != q.dtype:
         raise TypeError("Q, K, V, O, dO must share one dtype")
     return make_params(B, H, k.shape[1], N, d, _dtype_code(q), causal, scale, softcap, int(bool(deterministic)),
-                       window)
+                       window, dropout)
 
 
 def _check(status: int, where: str):
@@ -142,8 +152,9 @@ def _check(status: int, where: str):
         raise AttnError(status, where)
 
 
-def attn_fwd_stats(q, k, v, o, lse, *, causal=False, scale=None, softcap=0.0, stream=None, window=None):
-    p = _params_from(q, k, causal, scale, softcap, window=window)
+def attn_fwd_stats(q, k, v, o, lse, *, causal=False, scale=None, softcap=0.0, stream=None, window=None,
+                   dropout=None):
+    p = _params_from(q, k, causal, scale, softcap, window=window, dropout=dropout)
     lib = load_library()
     _check(lib.attn_fwd_stats(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(stream)),
            "attn_fwd_stats")
@@ -159,8 +170,8 @@ def attn_bwd_preprocess(o, do, D, dq_accum, *, H_kv=None, causal=False, scale=No
 
 
 def attn_bwd(q, k, v, do, lse, D, dq_accum, dk, dv, *, causal=False, scale=None, softcap=0.0, stream=None,
-             deterministic=False, window=None):
-    p = _params_from(q, k, causal, scale, softcap, deterministic, window)
+             deterministic=False, window=None, dropout=None):
+    p = _params_from(q, k, causal, scale, softcap, deterministic, window, dropout)
     lib = load_library()
     _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D),
                         _ptr(dq_accum), _ptr(dk), _ptr(dv), _stream(stream)), "attn_bwd")
@@ -174,19 +185,22 @@ def attn_bwd_dq_convert(dq_accum, dq, *, scale=None, stream=None):
            "attn_bwd_dq_convert")
 
 
-def attention_forward(q, k, v, *, causal=False, scale=None, softcap=0.0, stream=None, window=None):
-    """Returns (O, LSE) from attn_fwd_stats."""
+def attention_forward(q, k, v, *, causal=False, scale=None, softcap=0.0, stream=None, window=None, dropout=None):
+    """Returns (O, LSE) from attn_fwd_stats; dropout = (p, seed, offset) or None."""
     torch = _torch()
     B, H, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty(B, H, N, device=q.device, dtype=torch.float32)
-    attn_fwd_stats(q, k, v, o, lse, causal=causal, scale=scale, softcap=softcap, stream=stream, window=window)
+    attn_fwd_stats(q, k, v, o, lse, causal=causal, scale=scale, softcap=softcap, stream=stream, window=window,
+                   dropout=dropout)
     return o, lse
 
 
 def attention_backward(q, k, v, o, do, lse, *, causal=False, scale=None, softcap=0.0, stream=None,
-                       workspace=None, deterministic=False, window=None):
+                       workspace=None, deterministic=False, window=None, dropout=None):
     """Returns (dQ, dK, dV): preprocess -> bwd -> dq_convert on one stream.
+
+    ``dropout`` = (p, seed, offset) must be what the forward used.
 
     ``deterministic`` selects the atomic-free fp32 path (bf16 is atomic-free
     either way).
@@ -206,6 +220,6 @@ def attention_backward(q, k, v, o, do, lse, *, causal=False, scale=None, softcap
     attn_bwd_preprocess(o, do, D, acc, H_kv=k.shape[1], causal=causal, scale=scale, softcap=softcap, stream=stream,
                         window=window)
     attn_bwd(q, k, v, do, lse, D, acc, dk, dv, causal=causal, scale=scale, softcap=softcap, stream=stream,
-             deterministic=deterministic, window=window)
+             deterministic=deterministic, window=window, dropout=dropout)
     attn_bwd_dq_convert(acc, dq, scale=scale if scale is not None else d ** -0.5, stream=stream)
     return dq, dk, dv

@@ -27,6 +27,7 @@ int check_params(const attn_params* p, fabwd::Problem* out, bool* empty) {
   if (!std::isfinite(p->softcap) || p->softcap < 0.0f) return ATTN_ERR_INVALID_ARG;
   if (p->deterministic != 0 && p->deterministic != 1) return ATTN_ERR_INVALID_ARG;
   if (p->window_left < -1 || p->window_right < -1) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(p->dropout_p) || p->dropout_p < 0.0f || p->dropout_p >= 1.0f) return ATTN_ERR_INVALID_ARG;
   if (p->d != 64 && p->d != 128) return ATTN_ERR_UNSUPPORTED;
   if (p->N > kMaxN) return ATTN_ERR_INVALID_ARG;
   const int64_t elems = int64_t(p->B) * p->H * p->N * p->d;
@@ -47,6 +48,15 @@ int check_params(const attn_params* p, fabwd::Problem* out, bool* empty) {
     int wr = p->window_right < 0 ? n : std::min(p->window_right, n);
     if (p->causal) wr = std::min(wr, 0);
     out->wr = wr;
+  }
+  if (p->dropout_p > 0.0f) {
+    const double keep = std::floor((1.0 - double(p->dropout_p)) * 65536.0 + 0.5);
+    out->dropout = true;
+    out->keep_t = uint32_t(std::min(keep, 65536.0));
+    out->drop_scale = 1.0f / (1.0f - p->dropout_p);
+    out->seed_lo = p->rng_seed_lo;
+    out->seed_hi = p->rng_seed_hi;
+    out->rng_offset = p->rng_offset;
   }
   *empty = (p->B == 0 || p->N == 0);
   return ATTN_OK;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "philox.h"
+
 namespace fabwd {
 
 // Problem description shared by the launchers (already validated).
@@ -18,9 +20,16 @@ struct Problem {
   // Visible band: key k is visible to query q iff q - wl <= k <= q + wr (and
   // k < N).  Causal gives wr = 0; an unbounded side is N.
   int wl = 0, wr = 0;
+  // Dropout: kept iff the element's 16-bit Philox value is below keep_t;
+  // kept elements are scaled by drop_scale = 1 / (1 - p).
+  bool dropout = false;
+  uint32_t keep_t = 65536;
+  float drop_scale = 1.f;
+  uint32_t seed_lo = 0, seed_hi = 0, rng_offset = 0;
   int group() const { return H / H_kv; }
   int64_t q_rows() const { return int64_t(B) * H * N; }
   int64_t q_elems() const { return q_rows() * d; }
+  Dropout drop() const { return Dropout{dropout ? 1 : 0, keep_t, seed_lo, seed_hi, rng_offset, drop_scale}; }
 };
 
 hipError_t launch_fwd_stats(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,

@@ -13,6 +13,11 @@
 // exponentials are hardware exp2 with the log2(e) factor folded into the
 // scale.  The forward is the online-softmax loop of the Cookbook page,
 // section 3.1 (query blocks outer, key blocks inner).
+//
+// Dropout (FlashAttention-v1 page, section 3.3 and eqs (10)-(12)): each
+// element's keep bit is regenerated from the generator state (philox.h);
+// the forward accumulates P o Z into O while the row sum uses P, and the
+// backward uses P o Z for dV and (dO V^T) o Z for dP.
 #include "fabwd_device.h"
 #include "fabwd_launch.h"
 
@@ -30,7 +35,8 @@ template <typename T, int D, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                               const T* __restrict__ V, T* __restrict__ O,
                                                               float* __restrict__ LSE, int H, int H_kv, int N,
-                                                              float scale, float softcap, int wl, int wr) {
+                                                              float scale, float softcap, int wl, int wr,
+                                                              Dropout drop) {
   constexpr int BQ = 32, BK = 64, DX = D / 8;
   __shared__ float sQ[BQ][D];
   __shared__ float sK[BK][D + 1];
@@ -90,7 +96,10 @@ __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(const T* __restric
     for (int m = 0; m < BK / 8; ++m) {
       const float p = fast_exp2(z[m] - base);
       psum += p;
-      sP[r][sub + 8 * m] = p;
+      float pd = p;
+      if (drop.enabled)
+        pd = dropout_keep(drop, uint32_t(b * H + h), uint32_t(row), uint32_t(k0 + sub + 8 * m)) ? p * drop.scale : 0.f;
+      sP[r][sub + 8 * m] = pd;
     }
     psum = wave_xor_sum(psum, 8);
     l_run = l_run * alpha + psum;
@@ -123,7 +132,8 @@ __global__ __launch_bounds__(kThreads) void bwd_simple_kernel(const T* __restric
                                                               const float* __restrict__ Dv,
                                                               float* __restrict__ dQacc, T* __restrict__ dK,
                                                               T* __restrict__ dV, int H, int H_kv, int N,
-                                                              float scale, float softcap, int wl, int wr) {
+                                                              float scale, float softcap, int wl, int wr,
+                                                              Dropout drop) {
   constexpr int BK = 32, BQ = 32, DX = D / 8;
   __shared__ float sK[BK][D + 1];
   __shared__ float sV[BK][D + 1];
@@ -188,8 +198,11 @@ __global__ __launch_bounds__(kThreads) void bwd_simple_kernel(const T* __restric
         }
         const bool masked = key >= N || row >= N || key > row + wr || key < row - wl;
         const float p = masked ? 0.f : fast_exp2(s * zscale - sL[r]);
-        sP[r][c] = p;
-        sdS[r][c] = p * (dp - sD[r]) * dtanh;
+        float zd = 1.f;  // dropout multiplier Z of this element
+        if (drop.enabled)
+          zd = dropout_keep(drop, uint32_t(b * H + h), uint32_t(row), uint32_t(key)) ? drop.scale : 0.f;
+        sP[r][c] = p * zd;
+        sdS[r][c] = p * (dp * zd - sD[r]) * dtanh;
       }
       __syncthreads();
       // dV += P^T dO and dK += dS^T Q for key r (this thread's key row).
@@ -238,7 +251,7 @@ template <typename T, int D, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads) void bwd_dq_simple_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dv, float* __restrict__ dQacc, int H, int H_kv, int N,
-    float scale, float softcap, int wl, int wr) {
+    float scale, float softcap, int wl, int wr, Dropout drop) {
   constexpr int BQ = 32, BK = 32, DX = D / 8;
   __shared__ float sQ[BQ][D + 1];
   __shared__ float sdO[BQ][D + 1];
@@ -294,7 +307,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_simple_kernel(
       }
       const bool masked = key >= N || row >= N || key > row + wr || key < row - wl;
       const float p = masked ? 0.f : fast_exp2(s * zscale - lse2);
-      sdS[r][c] = p * (dp - dval) * dtanh;
+      float zd = 1.f;
+      if (drop.enabled) zd = dropout_keep(drop, uint32_t(b * H + h), uint32_t(row), uint32_t(key)) ? drop.scale : 0.f;
+      sdS[r][c] = p * (dp * zd - dval) * dtanh;
     }
     __syncthreads();
 #pragma unroll
@@ -317,7 +332,7 @@ hipError_t fwd_simple_t(const Problem& p, const void* Q, const void* K, const vo
   dim3 grid((p.N + 31) / 32, p.H, p.B);
   hipLaunchKernelGGL((fwd_simple_kernel<T, D, S>), grid, dim3(kThreads), 0, s, static_cast<const T*>(Q),
                      static_cast<const T*>(K), static_cast<const T*>(V), static_cast<T*>(O), LSE, p.H, p.H_kv,
-                     p.N, p.scale, p.softcap, p.wl, p.wr);
+                     p.N, p.scale, p.softcap, p.wl, p.wr, p.drop());
   return hipGetLastError();
 }
 
@@ -328,7 +343,7 @@ hipError_t bwd_simple_t(const Problem& p, const void* Q, const void* K, const vo
   auto kern = p.deterministic ? bwd_simple_kernel<T, D, S, false> : bwd_simple_kernel<T, D, S, true>;
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, static_cast<const T*>(Q), static_cast<const T*>(K),
                      static_cast<const T*>(V), static_cast<const T*>(dO), LSE, Dv, dQacc, static_cast<T*>(dK),
-                     static_cast<T*>(dV), p.H, p.H_kv, p.N, p.scale, p.softcap, p.wl, p.wr);
+                     static_cast<T*>(dV), p.H, p.H_kv, p.N, p.scale, p.softcap, p.wl, p.wr, p.drop());
   return hipGetLastError();
 }
 
@@ -338,7 +353,7 @@ hipError_t bwd_dq_simple_t(const Problem& p, const void* Q, const void* K, const
   dim3 grid((p.N + 31) / 32, p.H, p.B);
   hipLaunchKernelGGL((bwd_dq_simple_kernel<T, D, S>), grid, dim3(kThreads), 0, s, static_cast<const T*>(Q),
                      static_cast<const T*>(K), static_cast<const T*>(V), static_cast<const T*>(dO), LSE, Dv,
-                     dQacc, p.H, p.H_kv, p.N, p.scale, p.softcap, p.wl, p.wr);
+                     dQacc, p.H, p.H_kv, p.N, p.scale, p.softcap, p.wl, p.wr, p.drop());
   return hipGetLastError();
 }
 

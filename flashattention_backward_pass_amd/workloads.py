@@ -34,6 +34,7 @@ class Workload:
     sigma_qk: float     # standard deviation of Q and K entries (V and dO: 1)
     seed: int
     window: tuple = (-1, -1)  # local mask (window_left, window_right); -1 = unbounded side
+    dropout: tuple = None     # (p, seed, offset) of the dropout mask, or None
 
     @property
     def torch_dtype(self):
@@ -69,8 +70,9 @@ class Workload:
         return asdict(self)
 
 
-def _wl(name, B, H, H_kv, N, d, dtype, causal, softcap, sigma_qk, seed, window=(-1, -1)):
-    return Workload(name, B, H, H_kv, N, d, dtype, causal, softcap, 1.0 / math.sqrt(d), sigma_qk, seed, window)
+def _wl(name, B, H, H_kv, N, d, dtype, causal, softcap, sigma_qk, seed, window=(-1, -1), dropout=None):
+    return Workload(name, B, H, H_kv, N, d, dtype, causal, softcap, 1.0 / math.sqrt(d), sigma_qk, seed, window,
+                    dropout)
 
 
 # The workloads of the parity and performance suite.
@@ -86,16 +88,21 @@ WORKLOADS = {
         # itself and the 2048 keys before it.
         _wl("bf16_local2048_causal_b1h8_n16384_d128", 1, 8, 8, 16384, 128, "bf16", True, 0.0, 1.0, 1005,
             (2048, -1)),
+        # Dropout variant of the long workload: p = 0.1, generator seed and
+        # offset fixed.
+        _wl("bf16_dropout0.1_causal_b1h8_n16384_d128", 1, 8, 8, 16384, 128, "bf16", True, 0.0, 1.0, 1006,
+            dropout=(0.1, 0x5EED0000_00001006, 0)),
     ]
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
 
 def custom(B, H, H_kv, N, d, dtype="bf16", causal=False, softcap=0.0, tau=None, sigma_qk=1.0, seed=0,
-           name="custom", window=(-1, -1)) -> Workload:
+           name="custom", window=(-1, -1), dropout=None) -> Workload:
     """A workload of any shape, for edge-case tests (ragged N, tiny sizes, ...)."""
     return Workload(name, B, H, H_kv, N, d, dtype, causal, float(softcap),
-                    float(tau) if tau is not None else 1.0 / math.sqrt(d), sigma_qk, seed, tuple(window))
+                    float(tau) if tau is not None else 1.0 / math.sqrt(d), sigma_qk, seed, tuple(window),
+                    tuple(dropout) if dropout is not None else None)
 
 
 def make_inputs(w: Workload):

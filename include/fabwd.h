@@ -8,7 +8,8 @@
  *         dK scaled by the softmax scale), 3.1 (KV-block-outer loop), 6.2 (dQ
  *         accumulated with atomics into an fp32 dQaccum buffer), 8.5 (GQA).
  *   [FA1] "解析 FlashAttention（3）：FlashAttention-v1 反向传播" (FlashAttention-v1
- *         backward): equations (1)-(16) and Algorithm 4 (section 4).
+ *         backward): equations (1)-(16), section 3.3 (dropout replay) and
+ *         Algorithm 4 (section 4).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -35,6 +36,21 @@
  *    window_left >= 0, key j is masked for query i when j < i - window_left;
  *    with window_right >= 0, when j > i + window_right.  Both combine with
  *    the causal mask; -1 leaves a side unbounded, so (-1, -1) is no window.
+ *  - Dropout ([FA1] 3.3 and the dropout lines of Algorithm 4): with
+ *    dropout_p > 0 the forward multiplies P by a mask Z before P V, and the
+ *    backward regenerates the same Z from (rng_seed, rng_offset) instead of
+ *    storing it.  Z_ij = 1 / (1 - dropout_p) when element (i, j) is kept,
+ *    else 0.  The pages fix no generator; this library's is Philox4x32-10
+ *    (Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11):
+ *    for query head bh = b * H + h, query i and key j, one call with
+ *      counter = (j >> 1, i >> 2, bh, rng_offset),
+ *      key     = (rng_seed_lo, rng_seed_hi)
+ *    gives words x0..x3; u = bits [16 (j & 1), 16 (j & 1) + 16) of word
+ *    x[i & 3]; the element is kept iff u < t, t = floor((1 - p) 65536 + 1/2)
+ *    computed in double from the float dropout_p.  LSE is that of the
+ *    undropped P.  The same (seed, offset, dropout_p) must be passed to
+ *    attn_fwd_stats and attn_bwd; callers advance rng_offset (or the seed)
+ *    between layers and steps.
  *  - Every pointer must be 16-byte aligned.  Sizes with B*H*N*d beyond
  *    2^40 elements are rejected.  N = 0 or B = 0 is a valid empty problem:
  *    the call validates its arguments and enqueues nothing.
@@ -52,7 +68,8 @@ extern "C" {
 
 enum attn_status {
   ATTN_OK = 0,
-  ATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, H % H_kv != 0, scale <= 0, softcap < 0, window < -1, ... */
+  ATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, H % H_kv != 0, scale <= 0, softcap < 0, window < -1,
+                               dropout_p outside [0, 1), ... */
   ATTN_ERR_UNSUPPORTED = 2, /* no kernel instance for this (dtype, d) */
   ATTN_ERR_MISALIGNED = 3,  /* a pointer is not 16-byte aligned */
   ATTN_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
@@ -69,14 +86,19 @@ typedef struct attn_params {
   int32_t deterministic;    /* 0 or 1; see attn_bwd */
   int32_t window_left;      /* local mask: key j hidden from query i when j < i - window_left; -1 = off */
   int32_t window_right;     /* local mask: key j hidden from query i when j > i + window_right; -1 = off */
+  float dropout_p;          /* dropout probability in [0, 1); 0 = no dropout */
+  uint32_t rng_seed_lo;     /* dropout generator key, low word */
+  uint32_t rng_seed_hi;     /* dropout generator key, high word */
+  uint32_t rng_offset;      /* dropout generator counter word 3 (per call site / step) */
 } attn_params;
 
 /* Supported head dimensions: d = 64 and d = 128, for both dtypes. */
 
 /*
  * attn_fwd_stats - forward pass producing what the backward needs ([CB] 1.3).
- *   O[b,h,i,:]  = sum_j P_ij V[b,g,j,:],  P_i = softmax_j(Z_ij)   (dtype)
+ *   O[b,h,i,:]  = sum_j P_ij Zd_ij V[b,g,j,:],  P_i = softmax_j(Z_ij)   (dtype)
  *   LSE[b,h,i]  = ln sum_j exp(Z_ij)                             (float32, natural log)
+ * Zd is the dropout mask (all ones when dropout_p = 0).
  * Reads Q, K, V; writes O and LSE.
  */
 int attn_fwd_stats(const attn_params* p, const void* Q, const void* K, const void* V,
@@ -96,11 +118,13 @@ int attn_bwd_preprocess(const attn_params* p, const void* O, const void* dO,
  * attn_bwd - the recompute-based backward ([FA1] Algorithm 4; [CB] 3.1, 5.2).
  * For every key/value block j (outer) and query block i (inner):
  *   P   = exp(Z - LSE)                ([CB] 1.2)
- *   dV += P^T dO                      ([FA1] eq (10))
- *   dP  = dO V^T                      ([FA1] eq (11))
+ *   dV += (P o Zd)^T dO               ([FA1] eq (10))
+ *   dP  = (dO V^T) o Zd               ([FA1] eqs (11), (12))
  *   dS  = P o (dP - D), times (1 - tanh^2(R/c)) with a cap   ([FA1] eq (14); [CB] 2.1)
  *   dK += dS^T Q, scaled by `scale` once at the end            ([FA1] eq (16); [CB] 2.1)
  *   dQaccum += dS K (unscaled)                                 ([FA1] eq (15))
+ * Zd is the dropout mask regenerated from the generator state in `p` (all
+ * ones when dropout_p = 0); it must be the state attn_fwd_stats used.
  * Inputs: Q, K, V, dO (dtype), LSE from attn_fwd_stats, D from
  * attn_bwd_preprocess on the same stream.  dK and dV are overwritten (not
  * accumulated into).  dQaccum receives sum_j dS_ij K_j without the scale;

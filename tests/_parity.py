@@ -30,7 +30,8 @@ def run_gpu(w, x, *, o=None, lse=None, poison=False, deterministic=False):
     dev = torch.device("cuda:0")
     q, k, v, do = (x[n].to(dev) for n in ("Q", "K", "V", "dO"))
     if o is None:
-        o, lse = fab.attention_forward(q, k, v, causal=w.causal, scale=w.tau, softcap=w.softcap, window=w.window)
+        o, lse = fab.attention_forward(q, k, v, causal=w.causal, scale=w.tau, softcap=w.softcap, window=w.window,
+                                       dropout=w.dropout)
     else:
         o, lse = o.to(dev), lse.to(dev)
     B, H, N, d = q.shape
@@ -43,7 +44,7 @@ def run_gpu(w, x, *, o=None, lse=None, poison=False, deterministic=False):
     fab.attn_bwd_preprocess(o, do, D, acc, H_kv=w.H_kv, causal=w.causal, scale=w.tau, softcap=w.softcap,
                             window=w.window)
     fab.attn_bwd(q, k, v, do, lse, D, acc, dk, dv, causal=w.causal, scale=w.tau, softcap=w.softcap,
-                 deterministic=deterministic, window=w.window)
+                 deterministic=deterministic, window=w.window, dropout=w.dropout)
     acc_copy = acc.clone()
     fab.attn_bwd_dq_convert(acc, dq, scale=w.tau)
     torch.cuda.synchronize()
@@ -51,7 +52,7 @@ def run_gpu(w, x, *, o=None, lse=None, poison=False, deterministic=False):
 
 
 def oracle_full(w, x):
-    return oracle.reference(x["Q"], x["K"], x["V"], x["dO"], w.tau, w.causal, w.softcap, w.window)
+    return oracle.reference(x["Q"], x["K"], x["V"], x["dO"], w.tau, w.causal, w.softcap, w.window, w.dropout)
 
 
 def oracle_kv_heads(w, x, b, kv_heads):
@@ -63,8 +64,9 @@ def oracle_kv_heads(w, x, b, kv_heads):
         dk = dv = 0.0
         for h in range(g * G, (g + 1) * G):
             q, do = x["Q"][b, h], x["dO"][b, h]
-            O, L = oracle.forward_head(q, k, v, w.tau, w.causal, w.softcap, w.window)
-            dq, dk_h, dv_h, D = oracle.backward_head(q, k, v, O, do, L, w.tau, w.causal, w.softcap, w.window)
+            zf = oracle.head_dropout(w.dropout, b * w.H + h)
+            O, L = oracle.forward_head(q, k, v, w.tau, w.causal, w.softcap, w.window, zf)
+            dq, dk_h, dv_h, D = oracle.backward_head(q, k, v, O, do, L, w.tau, w.causal, w.softcap, w.window, zf)
             out["O"][h], out["LSE"][h], out["D"][h], out["dQ"][h] = O, L, D, dq
             dk = dk + dk_h
             dv = dv + dv_h

@@ -57,9 +57,10 @@ def test_params_layout_matches_header():
     text = open(HEADER).read()
     body = text[text.index("typedef struct attn_params {"):text.index("} attn_params;")]
     fields = []
-    for typ, names in re.findall(r"^\s*(int32_t|float)\s+([^;]+);", body, re.M):
+    types = {"int32_t": ctypes.c_int32, "uint32_t": ctypes.c_uint32, "float": ctypes.c_float}
+    for typ, names in re.findall(r"^\s*(u?int32_t|float)\s+([^;]+);", body, re.M):
         for n in names.split(","):
-            fields.append((n.strip(), ctypes.c_int32 if typ == "int32_t" else ctypes.c_float))
+            fields.append((n.strip(), types[typ]))
     assert [(n, t) for n, t in fab.attn_params._fields_] == fields
     assert ctypes.sizeof(fab.attn_params) == 4 * len(fields)  # no padding
 
@@ -86,13 +87,15 @@ BAD = [
     dict(causal=2), dict(scale=0.0), dict(scale=-1.0), dict(scale=float("nan")), dict(scale=float("inf")),
     dict(softcap=-1.0), dict(softcap=float("inf")), dict(N=(1 << 24) + 1),
     dict(window_left=-2), dict(window_right=-3),
+    dict(dropout_p=-0.1), dict(dropout_p=1.0), dict(dropout_p=1.5), dict(dropout_p=float("nan")),
+    dict(dropout_p=float("inf")),
 ]
 
 
 @pytest.mark.parametrize("bad", BAD, ids=[str(b) for b in BAD])
 def test_invalid_arguments(lib, bad):
     kw = dict(B=1, H=4, H_kv=2, N=64, d=64, dtype=1, causal=0, scale=0.125, softcap=0.0, deterministic=0,
-              window_left=-1, window_right=-1)
+              window_left=-1, window_right=-1, dropout_p=0.0, rng_seed_lo=0, rng_seed_hi=0, rng_offset=0)
     kw.update(bad)
     p = fab.attn_params(**kw)
     assert call_all(lib, p) == [fab.ATTN_ERR_INVALID_ARG] * 4
@@ -153,3 +156,17 @@ def test_windows_accepted(lib, window):
     # Valid windows on an empty problem: every argument is checked, nothing runs.
     p = fab.make_params(1, 2, 2, 0, 64, 1, causal=1, window=window)
     assert call_all(lib, p, ptr=None) == [fab.ATTN_OK] * 4
+
+
+@pytest.mark.parametrize("p", [0.0, 0.1, 0.999])
+def test_dropout_accepted(lib, p):
+    params = fab.make_params(1, 2, 2, 0, 64, 1, dropout=(p, (1 << 64) - 1, (1 << 32) - 1))
+    assert (params.rng_seed_lo, params.rng_seed_hi, params.rng_offset) == (0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF)
+    assert call_all(lib, params, ptr=None) == [fab.ATTN_OK] * 4
+
+
+def test_dropout_seed_range():
+    with pytest.raises(ValueError):
+        fab.make_params(1, 2, 2, 8, 64, 1, dropout=(0.1, 1 << 64, 0))
+    with pytest.raises(ValueError):
+        fab.make_params(1, 2, 2, 8, 64, 1, dropout=(0.1, 0, 1 << 32))
