@@ -97,8 +97,9 @@ def cpu_baseline(w, x, heads=3):
     for h in range(heads):
         q, do = x["Q"][0, h], x["dO"][0, h]
         k, v = x["K"][0, h // group], x["V"][0, h // group]
-        O, L = oracle.forward_head(q, k, v, w.tau, w.causal, w.softcap, w.window)
-        oracle.backward_head(q, k, v, O, do, L, w.tau, w.causal, w.softcap, w.window)
+        zf = oracle.head_dropout(w.dropout, h)
+        O, L = oracle.forward_head(q, k, v, w.tau, w.causal, w.softcap, w.window, zf)
+        oracle.backward_head(q, k, v, O, do, L, w.tau, w.causal, w.softcap, w.window, zf)
     dt = time.perf_counter() - t0
     flops = heads * w.flops() / (w.B * w.H)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
@@ -127,7 +128,7 @@ def main():
     dev = torch.device("cuda:0")
     q, k, v, do = (x[n].to(dev) for n in ("Q", "K", "V", "dO"))
     kw = dict(causal=w.causal, scale=w.tau, softcap=w.softcap, window=w.window)
-    o, lse = fab.attention_forward(q, k, v, **kw)
+    o, lse = fab.attention_forward(q, k, v, dropout=w.dropout, **kw)
     B, H, N, d = q.shape
     D = torch.empty(B, H, N, device=dev, dtype=torch.float32)
     acc = torch.empty(B, H, N, d, device=dev, dtype=torch.float32)
@@ -140,7 +141,7 @@ def main():
         fab.attn_bwd_preprocess(o, do, D, acc, H_kv=w.H_kv, **kw)
         if ev is not None:
             ev[1].record()
-        fab.attn_bwd(q, k, v, do, lse, D, acc, dk, dv, **kw)
+        fab.attn_bwd(q, k, v, do, lse, D, acc, dk, dv, dropout=w.dropout, **kw)
         if ev is not None:
             ev[2].record()
         fab.attn_bwd_dq_convert(acc, dq, scale=w.tau)
@@ -167,7 +168,7 @@ def main():
     fe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     fe[0].record()
     for _ in range(5):
-        fab.attn_fwd_stats(q, k, v, o, lse, **kw)
+        fab.attn_fwd_stats(q, k, v, o, lse, dropout=w.dropout, **kw)
     fe[1].record()
     torch.cuda.synchronize()
     fwd_ms = fe[0].elapsed_time(fe[1]) / 5
@@ -195,7 +196,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded iid normal Q, K, V, dO; O and LSE from attn_fwd_stats)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "N": w.N, "d": w.d,
-                   "causal": w.causal, "softcap": w.softcap, "tau": w.tau, "parallelism": "single GPU"},
+                   "causal": w.causal, "softcap": w.softcap, "tau": w.tau, "window": list(w.window),
+                   "dropout_p": w.dropout[0] if w.dropout else 0.0, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(bwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,

@@ -39,6 +39,14 @@
 //   rescales the LSE of tile t+1 in LDS during C(1); then wait + barrier.
 // The loop is unrolled over the two buffers so every LDS offset is a
 // compile-time immediate.
+//
+// Dropout (FlashAttention-v1 page, section 3.3, eqs (10)-(12)): the mask of
+// each 32-query half is regenerated during its A stage (the 10 generator
+// rounds are spread over the slots; lanes l and l^1 share the calls, see
+// philox.h).  The dP accumulator then starts at 0 (acc = -dP~, dP~ = dO V^T),
+// and -dS = P (D + Z acc) with Z = 1/(1-p) or 0, D read from LDS one step
+// ahead; dV accumulates (P o keep)^T dO and takes the 1/(1-p) in the
+// epilogue.
 #include <type_traits>
 
 #include "fabwd_launch.h"
@@ -56,16 +64,17 @@ constexpr int BR = 64;   // query rows per inner iteration
 struct Cursor {
   int q0;        // first row of the query block
   int64_t row0;  // (b*H + h)*N, row offset of the query head
+  int bh;        // b*H + h, the query head (dropout generator counter)
 };
 
 // Key k is visible to query q iff q - wl <= k <= q + wr and k < N (causal:
 // wr = 0; an unbounded side is N).
-template <int D, bool SOFTCAP>
+template <int D, bool SOFTCAP, bool DROPOUT>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int H, int H_kv, int N, int BH, float scale,
-    float softcap, int wl, int wr, int n_split, float* __restrict__ part) {
+    float softcap, int wl, int wr, int n_split, float* __restrict__ part, Dropout drop) {
   constexpr int KC = D / 16;  // 16-wide k chunks over d
   constexpr int NT = D / 32;  // 32-wide column tiles over d
   // Double buffers as separate variables: the compiler gives each LDS
@@ -142,6 +151,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     if (c.q0 == i_lo * BR) {
       c.q0 = q_last;
       c.row0 += N;
+      ++c.bh;
     } else {
       c.q0 -= BR;
     }
@@ -220,7 +230,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // later slot, a share of the other work) separated by scheduling barriers,
   // so the compiler keeps this order and its register use stays bounded.
   // `next` is the tile whose copies go out during A(0), into the other buffer.
-  auto do_tile = [&](auto bufc, int q0, bool masked, const Cursor& next) {
+  auto do_tile = [&](auto bufc, int q0, int bh, bool masked, const Cursor& next) {
     using NB = std::integral_constant<int, 1 - decltype(bufc)::value>;
     const uint16_t* tq_ = bufsel(bufc, sQ0, sQ1);
     const uint16_t* to_ = bufsel(bufc, sdO0, sdO1);
@@ -273,9 +283,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         sa[r] = sa[r] * zs;
       }
     };
-    auto step2 = [&](f32x16_t& sa, int r) { sa[r] = fast_exp2(sa[r]); };
-    auto step3 = [&](f32x16_t& sa, f32x16_t& da, const f32x16_t& la, u32x4_t* pw, u32x4_t* dw, int r) {
-      float ds = sa[r] * da[r];
+    // With dropout, step 2 also fetches D of the element's query row.
+    auto step2 = [&](f32x16_t& sa, f32x16_t& dd, int h, int r) {
+      sa[r] = fast_exp2(sa[r]);
+      if (DROPOUT) dd[r] = sd_[32 * h + 8 * (r >> 2) + 4 * g + (r & 3)];
+    };
+    auto step3 = [&](f32x16_t& sa, f32x16_t& da, const f32x16_t& la, const f32x16_t& dd, const DropBits& kb,
+                     u32x4_t* pw, u32x4_t* dw, int r) {
+      float ds;
+      if (DROPOUT) {
+        const bool kp = kb.keep(r, drop.keep_t);
+        ds = sa[r] * fmaf(kp ? drop.scale : 0.f, da[r], dd[r]);
+        sa[r] = kp ? sa[r] : 0.f;
+      } else {
+        ds = sa[r] * da[r];
+      }
       if (SOFTCAP) ds *= la[r];
       da[r] = ds;
       if (r & 1) {
@@ -285,14 +307,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     };
     // Pipeline position `slot` of a stage with E elements per slot; slots past
     // the stage's own (16 / E) only drain steps 2 and 3.
-    auto sm_slot = [&](f32x16_t& sa, f32x16_t& da, f32x16_t& la, u32x4_t* pw, u32x4_t* dw, int E, int slot) {
+    auto sm_slot = [&](f32x16_t& sa, f32x16_t& da, f32x16_t& la, f32x16_t& dd, const DropBits& kb, int h,
+                       u32x4_t* pw, u32x4_t* dw, int E, int slot) {
       const int ns = 16 / E;
       if (slot < ns)
         for (int e = 0; e < E; ++e) step1(sa, la, E * slot + e);
       if (slot >= 1 && slot - 1 < ns)
-        for (int e = 0; e < E; ++e) step2(sa, E * (slot - 1) + e);
+        for (int e = 0; e < E; ++e) step2(sa, dd, h, E * (slot - 1) + e);
       if (slot >= 2 && slot - 2 < ns)
-        for (int e = 0; e < E; ++e) step3(sa, da, la, pw, dw, E * (slot - 2) + e);
+        for (int e = 0; e < E; ++e) step3(sa, da, la, dd, kb, pw, dw, E * (slot - 2) + e);
+    };
+    // Mask generator of one half: init, then rounds spread over the KC slots
+    // of its A stage, then the lane-pair exchange.
+    DropKeyLane gen;
+    DropBits kb0, kb1;
+    f32x16_t dd0, dd1;
+    auto gen_slot = [&](int c) {
+      if (DROPOUT) gen.rounds(10 * c / KC, 10 * (c + 1) / KC);
     };
 
     constexpr int PF = 2;              // row-operand prefetch distance (chunks)
@@ -305,7 +336,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     // ---- A(0), with the copies of the next tile ----
     s0 = SOFTCAP ? f32x16_t{} : acc_init(sl_, 0);
     if (SOFTCAP) l0 = acc_init(sl_, 0);
-    d0 = acc_init(sd_, 0);
+    d0 = DROPOUT ? f32x16_t{} : acc_init(sd_, 0);
+    if (DROPOUT) gen.init(drop, uint32_t(bh), q0, my_key, lane);
     if (masked) mask_init(SOFTCAP ? l0 : s0, 0);
 #pragma unroll
     for (int c = 0; c < PF; ++c) {
@@ -328,11 +360,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       d0 = mfma32(oa[c], vreg[c], d0);
 #pragma unroll
       for (int k = c; k < NDMA; k += KC) copy_one(NB{}, next, k);
+      gen_slot(c);
       __builtin_amdgcn_sched_barrier(0);
     }
     s1 = SOFTCAP ? f32x16_t{} : acc_init(sl_, 1);
     if (SOFTCAP) l1 = acc_init(sl_, 1);
-    d1 = acc_init(sd_, 1);
+    d1 = DROPOUT ? f32x16_t{} : acc_init(sd_, 1);
     if (masked) mask_init(SOFTCAP ? l1 : s1, 1);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -345,7 +378,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       }
       s1 = mfma32(qa[c], kreg[c], s1);
       d1 = mfma32(oa[c], vreg[c], d1);
-      sm_slot(s0, d0, l0, pw0, dw0, EA, c);
+      if (DROPOUT && c == 0) {
+        kb0 = gen.finish(lane);
+        gen.init(drop, uint32_t(bh), q0 + 32, my_key, lane);
+      }
+      gen_slot(c);
+      sm_slot(s0, d0, l0, dd0, kb0, 0, pw0, dw0, EA, c);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -367,8 +405,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       dv_acc[n] = mfma32(__builtin_bit_cast(bf16x8_t, pw0[u]), ob[i & 1], dv_acc[n]);
       dk_acc[n] = mfma32(__builtin_bit_cast(bf16x8_t, dw0[u]), qb[i & 1], dk_acc[n]);
       // Drain B(0) in the first two slots; B(1) runs alongside.
-      if (i < 2) sm_slot(s0, d0, l0, pw0, dw0, EA, KC + i);
-      sm_slot(s1, d1, l1, pw1, dw1, EC, i);
+      if (DROPOUT && i == 0) kb1 = gen.finish(lane);
+      if (i < 2) sm_slot(s0, d0, l0, dd0, kb0, 0, pw0, dw0, EA, KC + i);
+      sm_slot(s1, d1, l1, dd1, kb1, 1, pw1, dw1, EC, i);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -382,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       }
       dv_acc[n] = mfma32(__builtin_bit_cast(bf16x8_t, pw1[u]), ob[i & 1], dv_acc[n]);
       dk_acc[n] = mfma32(__builtin_bit_cast(bf16x8_t, dw1[u]), qb[i & 1], dk_acc[n]);
-      if (i < 2) sm_slot(s1, d1, l1, pw1, dw1, EC, 2 * NT + i);
+      if (i < 2) sm_slot(s1, d1, l1, dd1, kb1, 1, pw1, dw1, EC, 2 * NT + i);
       if (i == 2) prescale(NB{});
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -405,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     }
     __syncthreads();
   }
-  Cursor cc{q_last, head0};  // tile being computed
+  Cursor cc{q_last, head0, int(b) * H + (hk * n_split + split) * G};  // tile being computed
   Cursor ci = cc;            // tile being copied
   {
 #pragma unroll
@@ -420,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     __syncthreads();  // tile t in this buffer; the other buffer no longer read
     // After the last tile the copy repeats the current tile into the idle
     // buffer, which nothing reads: no branch around the copies.
-    do_tile(bufc, cc.q0, masked, t + 1 < n_iter ? ci : cc);
+    do_tile(bufc, cc.q0, cc.bh, masked, t + 1 < n_iter ? ci : cc);
     advance(ci);
     advance(cc);
   };
@@ -433,6 +472,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // (rows = keys, lanes = d); with a head split, the raw fp32 accumulators
   // go to `part` ([2][n_split][B*H_kv*N][D]: dK partials, then dV partials).
   const int64_t plane = int64_t(BH) * N * D;
+  const float v_scale = DROPOUT ? drop.scale : 1.f;  // dV sums P o keep; Z = keep / (1 - p)
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
 #pragma unroll
@@ -442,10 +482,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         const int64_t off = (kv_off + key) * D + 32 * n + l32;
         if (n_split == 1) {
           dK[off].bits = f32_to_bf16(dk_acc[n][r] * -scale);
-          dV[off].bits = f32_to_bf16(dv_acc[n][r]);
+          dV[off].bits = f32_to_bf16(dv_acc[n][r] * v_scale);
         } else {
           part[split * plane + off] = dk_acc[n][r];
-          part[(n_split + split) * plane + off] = dv_acc[n][r];
+          part[(n_split + split) * plane + off] = dv_acc[n][r] * v_scale;
         }
       }
     }
@@ -485,7 +525,7 @@ __global__ __launch_bounds__(256) void dkdv_split_sum_kernel(const float* __rest
   *reinterpret_cast<u32x4_t*>(dV + i) = vo;
 }
 
-template <int D, bool SOFTCAP>
+template <int D, bool SOFTCAP, bool DROPOUT>
 hipError_t dkdv_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                   const float* Dv, void* dK, void* dV, float* scratch, hipStream_t s) {
   const int BH = p.B * p.H_kv;
@@ -497,11 +537,11 @@ hipError_t dkdv_t(const Problem& p, const void* Q, const void* K, const void* V,
   // when G >= 4.
   const int G = p.H / p.H_kv;
   const int n_split = (scratch != nullptr && G >= 4 && int64_t(BH) * n_kblk < 1024) ? 2 : 1;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, SOFTCAP>), dim3(unsigned(BH) * unsigned(n_kblk) * unsigned(n_split)),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, SOFTCAP, DROPOUT>), dim3(unsigned(BH) * unsigned(n_kblk) * unsigned(n_split)),
                      dim3(kThreads), 0, s, static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K),
                      static_cast<const bf16_t*>(V), static_cast<const bf16_t*>(dO), LSE, Dv,
                      static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV), p.H, p.H_kv, p.N, BH, p.scale, p.softcap,
-                     p.wl, p.wr, n_split, n_split > 1 ? scratch : nullptr);
+                     p.wl, p.wr, n_split, n_split > 1 ? scratch : nullptr, p.drop());
   if (n_split == 1) return hipGetLastError();
   const int64_t elems = int64_t(BH) * p.N * D;
   const unsigned blocks = unsigned((elems / 8 + 255) / 256);
@@ -513,8 +553,11 @@ hipError_t dkdv_t(const Problem& p, const void* Q, const void* K, const void* V,
 template <int D>
 hipError_t dkdv_d(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                   const float* Dv, void* dK, void* dV, float* scratch, hipStream_t s) {
-  return p.softcap > 0.f ? dkdv_t<D, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s)
-                         : dkdv_t<D, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s);
+  if (p.dropout)
+    return p.softcap > 0.f ? dkdv_t<D, true, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s)
+                           : dkdv_t<D, false, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s);
+  return p.softcap > 0.f ? dkdv_t<D, true, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s)
+                         : dkdv_t<D, false, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s);
 }
 
 }  // namespace

@@ -22,6 +22,9 @@
 //                      lanes; K^T read transposed from the row-major K tile)
 // Computing S^T rather than S puts one query per lane, so LSE and D are one
 // register each.
+// Dropout (FlashAttention-v1 page, eq (12)): dP^T is multiplied by the
+// replayed mask Z before dS; the quad of lanes holding 4 consecutive queries
+// evaluates the 8 generator calls of a 32-key half together (philox.h).
 #include "fabwd_launch.h"
 #include "mfma_common.h"
 
@@ -35,11 +38,12 @@ constexpr int BK = 64;   // keys per inner step
 
 // Key k is visible to query q iff q - wl <= k <= q + wr and k < N (causal:
 // wr = 0; an unbounded side is N).
-template <int D, bool SOFTCAP>
+template <int D, bool SOFTCAP, bool DROPOUT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    float* __restrict__ dQacc, int H, int H_kv, int N, int BHq, float scale, float softcap, int wl, int wr) {
+    float* __restrict__ dQacc, int H, int H_kv, int N, int BHq, float scale, float softcap, int wl, int wr,
+    Dropout drop) {
   constexpr int KC = D / 16;
   constexpr int NT = D / 32;
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BK * D];
@@ -136,6 +140,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         st = mfma32(*reinterpret_cast<const bf16x8_t*>(&sK[buf][off]), qreg[c], st);
         dpt = mfma32(*reinterpret_cast<const bf16x8_t*>(&sV[buf][off]), doreg[c], dpt);
       }
+      DropBits keep;
+      if (DROPOUT) {
+        DropQueryLane gen;
+        gen.init(drop, uint32_t(bhq), kb + 32 * s, my_q, lane);
+        gen.rounds(0, 10);
+        keep = gen.finish(lane);
+      }
       // Register r: key kb + 32 s + 8(r/4) + 4g + r%4, query my_q.
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -151,7 +162,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           const int key = kb + 32 * s + 8 * (r >> 2) + 4 * g + (r & 3);
           if (key >= N || key > my_q + wr || key < my_q - wl) p = 0.f;
         }
-        float ds = p * (dpt[r] - dval);
+        float dp = dpt[r];
+        if (DROPOUT) dp = keep.keep(r, drop.keep_t) ? dp * drop.scale : 0.f;
+        float ds = p * (dp - dval);
         if (SOFTCAP) ds *= dt;
         st[r] = ds;
       }
@@ -185,23 +198,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-template <int D, bool SOFTCAP>
+template <int D, bool SOFTCAP, bool DROPOUT>
 hipError_t dq_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                 const float* Dv, float* dQacc, hipStream_t s) {
   const int BHq = p.B * p.H;
   const int n_qblk = (p.N + BQ - 1) / BQ;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, SOFTCAP>), dim3(unsigned(BHq) * unsigned(n_qblk)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, SOFTCAP, DROPOUT>), dim3(unsigned(BHq) * unsigned(n_qblk)), dim3(kThreads), 0, s,
                      static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V),
                      static_cast<const bf16_t*>(dO), LSE, Dv, dQacc, p.H, p.H_kv, p.N, BHq, p.scale, p.softcap,
-                     p.wl, p.wr);
+                     p.wl, p.wr, p.drop());
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t dq_d(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                 const float* Dv, float* dQacc, hipStream_t s) {
-  return p.softcap > 0.f ? dq_t<D, true>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
-                         : dq_t<D, false>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
+  if (p.dropout)
+    return p.softcap > 0.f ? dq_t<D, true, true>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
+                           : dq_t<D, false, true>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
+  return p.softcap > 0.f ? dq_t<D, true, false>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
+                         : dq_t<D, false, false>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
 }
 
 }  // namespace

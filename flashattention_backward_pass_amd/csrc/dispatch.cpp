@@ -7,7 +7,7 @@ hipError_t launch_fwd_stats(const Problem& p, const void* Q, const void* K, cons
                             hipStream_t s) {
   (void)hipGetLastError();
   // bf16: matrix-core kernel; fp32: vector-ALU kernel.
-  if (p.dtype == 1 && !p.dropout) return launch_fwd_mfma(p, Q, K, V, O, LSE, s);
+  if (p.dtype == 1) return launch_fwd_mfma(p, Q, K, V, O, LSE, s);
   return launch_fwd_simple(p, Q, K, V, O, LSE, s);
 }
 
@@ -15,13 +15,6 @@ hipError_t launch_bwd(const Problem& p, const void* Q, const void* K, const void
                       const float* LSE, const float* D, float* dQacc, void* dK, void* dV, hipStream_t s) {
   (void)hipGetLastError();
   // bf16: matrix-core kernels; fp32: vector-ALU kernel (same fp32 peak on MI355X).
-  if (p.dtype == 1 && p.dropout) {
-    Problem q = p;
-    q.deterministic = true;  // dQaccum is overwritten, not accumulated into
-    hipError_t e = launch_bwd_simple(q, Q, K, V, dO, LSE, D, dQacc, dK, dV, s);
-    if (e != hipSuccess) return e;
-    return launch_bwd_dq_simple(q, Q, K, V, dO, LSE, D, dQacc, s);
-  }
   if (p.dtype == 1) {
     // dQaccum is overwritten by the dQ kernel afterwards: until then the
     // dK/dV kernel may keep partial sums in it.

@@ -18,6 +18,10 @@
 // than 8 (log2 units) are O and the row sum rescaled, so P <= 2^8 and the
 // rescale is rare; O / l and LSE = (m + log2 l) ln 2 at the end are exact
 // whatever max was used.
+// Dropout (FlashAttention-v1 page, section 3.3): P^T is multiplied by the
+// mask Z before it enters O^T (the row sum keeps the undropped P); the mask
+// is regenerated per 32-key half from the generator state (philox.h), and
+// the 1 / (1 - p) of the kept elements is applied with the final 1 / l.
 #include <type_traits>
 
 #include "fabwd_launch.h"
@@ -35,11 +39,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // Key k is visible to query q iff q - wl <= k <= q + wr and k < N (causal:
 // wr = 0; an unbounded side is N).
-template <int D, bool SOFTCAP>
+template <int D, bool SOFTCAP, bool DROPOUT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     bf16_t* __restrict__ O, float* __restrict__ LSE, int H, int H_kv, int N, int BHq, float scale, float softcap,
-    int wl, int wr) {
+    int wl, int wr, Dropout drop) {
   constexpr int KC = D / 16;
   constexpr int NT = D / 32;
   // Double buffers as separate variables (own alias scopes: reads of one
@@ -155,6 +159,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       st = mfma32(*reinterpret_cast<const bf16x8_t*>(&sk[off_a[c] + 32 * s * D]), qreg[c], st);
     // Phases (S chain | softmax | O chain) stay in order: bounded live ranges.
     __builtin_amdgcn_sched_barrier(0);
+    // Mask bits of this half (the other wave's matrix instructions overlap).
+    DropBits keep;
+    if (DROPOUT) {
+      DropQueryLane gen;
+      gen.init(drop, uint32_t(bhq), kb + 32 * s, my_q, lane);
+      gen.rounds(0, 10);
+      keep = gen.finish(lane);
+    }
     // Scores in log2 units; new max over these keys and the partner lane's.
     float mx = -__builtin_inff();
 #pragma unroll
@@ -190,7 +202,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const float p0 = fast_exp2(st[8 * u + 2 * k] - mu);
         const float p1 = fast_exp2(st[8 * u + 2 * k + 1] - mu);
         l += p0 + p1;
-        pw[k] = pack_bf16x2(p0, p1);
+        if (DROPOUT)
+          pw[k] = pack_bf16x2(keep.keep(8 * u + 2 * k, drop.keep_t) ? p0 : 0.f,
+                              keep.keep(8 * u + 2 * k + 1, drop.keep_t) ? p1 : 0.f);
+        else
+          pw[k] = pack_bf16x2(p0, p1);
       }
       pf[u] = __builtin_bit_cast(bf16x8_t, pw);
     }
@@ -249,7 +265,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // register group), LSE = (m + log2 l) ln 2.
   l += __shfl_xor(l, 32);
   if (my_q < N) {
-    const float inv = 1.f / l;
+    const float inv = (DROPOUT ? drop.scale : 1.f) / l;
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -263,19 +279,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-template <int D, bool SOFTCAP>
+template <int D, bool SOFTCAP, bool DROPOUT>
 hipError_t fwd_t(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE, hipStream_t s) {
   const int BHq = p.B * p.H;
   const int n_qblk = (p.N + BQ - 1) / BQ;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, SOFTCAP>), dim3(unsigned(BHq) * unsigned(n_qblk)), dim3(kThreads), 0, s,
-                     static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V),
-                     static_cast<bf16_t*>(O), LSE, p.H, p.H_kv, p.N, BHq, p.scale, p.softcap, p.wl, p.wr);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, SOFTCAP, DROPOUT>), dim3(unsigned(BHq) * unsigned(n_qblk)), dim3(kThreads),
+                     0, s, static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K),
+                     static_cast<const bf16_t*>(V), static_cast<bf16_t*>(O), LSE, p.H, p.H_kv, p.N, BHq, p.scale,
+                     p.softcap, p.wl, p.wr, p.drop());
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t fwd_d(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE, hipStream_t s) {
-  return p.softcap > 0.f ? fwd_t<D, true>(p, Q, K, V, O, LSE, s) : fwd_t<D, false>(p, Q, K, V, O, LSE, s);
+  if (p.dropout)
+    return p.softcap > 0.f ? fwd_t<D, true, true>(p, Q, K, V, O, LSE, s) : fwd_t<D, false, true>(p, Q, K, V, O, LSE, s);
+  return p.softcap > 0.f ? fwd_t<D, true, false>(p, Q, K, V, O, LSE, s) : fwd_t<D, false, false>(p, Q, K, V, O, LSE, s);
 }
 
 }  // namespace
