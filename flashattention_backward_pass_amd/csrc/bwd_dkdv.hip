@@ -134,6 +134,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
   const float zs = scale * kLog2e;
   const float lse_mul = SOFTCAP ? kLog2e : -1.f / scale;
+  const float cap_k = SOFTCAP ? 2.f * kLog2e / softcap : 0.f;  // tanh(x / c) = tanh_scaled(x, cap_k)
+  const float cap_zs = softcap * zs;
   // Query blocks [i_lo, i_hi) hold every row that sees a key of this block.
   const int k_end = min(k0 + BC, N);
   const int i_lo = max(0, k0 - wr) / BR;
@@ -276,9 +278,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     //   3: -dS = P * dP_acc [* (1 - tanh^2)]; bf16 pairs packed
     auto step1 = [&](f32x16_t& sa, f32x16_t& la, int r) {
       if (SOFTCAP) {
-        const float th = tanh_f32(sa[r] / softcap);
-        sa[r] = fmaf(softcap * th, zs, -la[r]);
-        la[r] = 1.f - th * th;
+        const float th = tanh_scaled(sa[r], cap_k);
+        sa[r] = fmaf(cap_zs, th, -la[r]);
+        la[r] = fmaf(-th, th, 1.f);
       } else {
         sa[r] = sa[r] * zs;
       }

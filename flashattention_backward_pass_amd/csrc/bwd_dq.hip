@@ -77,6 +77,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float nl2 = -LSE[q_off + my_qc] * kLog2e;
   const float dval = Dv[q_off + my_qc];
   const float zs = scale * kLog2e;
+  const float cap_k = SOFTCAP ? 2.f * kLog2e / softcap : 0.f;  // tanh(x / c) = tanh_scaled(x, cap_k)
+  const float cap_zs = softcap * zs;
 
   f32x16_t dq_acc[NT];
 #pragma unroll
@@ -150,14 +152,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       // Register r: key kb + 32 s + 8(r/4) + 4g + r%4, query my_q.
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = st[r];
         float dt = 1.f;
+        float p;
         if (SOFTCAP) {
-          const float th = tanh_f32(x / softcap);
-          x = softcap * th;
-          dt = 1.f - th * th;
+          const float th = tanh_scaled(st[r], cap_k);
+          dt = fmaf(-th, th, 1.f);
+          p = fast_exp2(fmaf(th, cap_zs, nl2));
+        } else {
+          p = fast_exp2(fmaf(st[r], zs, nl2));
         }
-        float p = fast_exp2(fmaf(x, zs, nl2));
         if (masked) {
           const int key = kb + 32 * s + 8 * (r >> 2) + 4 * g + (r & 3);
           if (key >= N || key > my_q + wr || key < my_q - wl) p = 0.f;

@@ -52,12 +52,14 @@ struct Elem<bf16_t> {
 // Hardware 2^x (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// tanh from the identity tanh(|x|) = 1 - 2 / (2^(2|x| log2 e) + 1), sign restored
-// afterwards.  Saturates to +-1 for large |x| (2^big = inf, 2/inf = 0).
-__device__ __forceinline__ float tanh_f32(float x) {
-  float e = fast_exp2(2.0f * kLog2e * fabsf(x));
-  float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
-  return copysignf(t, x);
+// tanh(x / c) from the identity tanh(y) = 1 - 2 / (e^(2y) + 1), with
+// k = 2 log2(e) / c precomputed so there is no division per element:
+// e^(2x/c) = 2^(k x).  Odd-correct and saturating at both ends: 2^(k x)
+// overflows to inf for large x (tanh -> 1) and underflows to 0 for very
+// negative x (tanh -> -1).  Absolute error a few ulp of 1.
+__device__ __forceinline__ float tanh_scaled(float x, float k) {
+  const float e = fast_exp2(k * x);
+  return fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
 }
 
 __device__ __forceinline__ float wave_xor_sum(float v, int width) {

@@ -76,6 +76,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int c = 0; c < KC; ++c) qreg[c] = load_bf16x8(Q + (q_off + qc) * D + 16 * c + 8 * g);
   const float zs = scale * kLog2e;
+  const float cap_k = SOFTCAP ? 2.f * kLog2e / softcap : 0.f;  // tanh(x / c) = tanh_scaled(x, cap_k)
+  const float cap_zs = softcap * zs;
 
   f32x16_t o_acc[NT];  // O^T: register r of tile n = d index 32n + 8(r/4) + 4g + r%4
 #pragma unroll
@@ -173,8 +175,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int r = 0; r < 16; ++r) {
       float z = st[r];
       // The cap would turn a masked -inf into a finite -c: keep it -inf.
-      if (SOFTCAP) z = (MASKED && z == -__builtin_inff()) ? z : softcap * tanh_f32(z / softcap);
-      z *= zs;  // -inf stays -inf
+      if (SOFTCAP)
+        z = (MASKED && z == -__builtin_inff()) ? z : cap_zs * tanh_scaled(z, cap_k);
+      else
+        z *= zs;  // -inf stays -inf
       st[r] = z;
       mx = fmaxf(mx, z);
     }

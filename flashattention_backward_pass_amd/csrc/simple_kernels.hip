@@ -64,6 +64,7 @@ __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(const T* __restric
   const int kv_begin = max(0, q0 - wl) / BK * BK;
   const int kv_end = min(N, min(q0 + BQ, N) + wr);
   const float zscale = scale * kLog2e;
+  const float cap_k = SOFTCAP ? 2.f * kLog2e / softcap : 0.f;  // tanh(x / c) = tanh_scaled(x, cap_k)
   for (int k0 = kv_begin; k0 < kv_end; k0 += BK) {
     __syncthreads();
     for (int idx = t; idx < BK * D; idx += kThreads) {
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(const T* __restric
       float s = 0.f;
 #pragma unroll 8
       for (int x = 0; x < D; ++x) s = fmaf(sQ[r][x], sK[c][x], s);
-      if (SOFTCAP) s = softcap * tanh_f32(s / softcap);
+      if (SOFTCAP) s = softcap * tanh_scaled(s, cap_k);
       float zz = s * zscale;
       if (key >= N || key > row + wr || key < row - wl) zz = -INFINITY;
       z[m] = zz;
@@ -106,11 +107,12 @@ __global__ __launch_bounds__(kThreads) void fwd_simple_kernel(const T* __restric
     m_run = m_new;
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < DX; ++k) {
-      const int x = sub + 8 * k;
-      float a = acc[k] * alpha;
-      for (int c = 0; c < BK; ++c) a = fmaf(sP[r][c], sV[c][x], a);
-      acc[k] = a;
+    for (int k = 0; k < DX; ++k) acc[k] *= alpha;
+#pragma unroll 2
+    for (int c = 0; c < BK; ++c) {
+      const float pv = sP[r][c];
+#pragma unroll
+      for (int k = 0; k < DX; ++k) acc[k] = fmaf(pv, sV[c][sub + 8 * k], acc[k]);
     }
   }
   if (row < N) {
@@ -160,6 +162,7 @@ __global__ __launch_bounds__(kThreads) void bwd_simple_kernel(const T* __restric
   for (int k = 0; k < DX; ++k) acc_dk[k] = acc_dv[k] = 0.f;
 
   const float zscale = scale * kLog2e;
+  const float cap_k = SOFTCAP ? 2.f * kLog2e / softcap : 0.f;  // tanh(x / c) = tanh_scaled(x, cap_k)
   // Query rows that see some key of the block.
   const int q_begin = max(0, k0 - wr) / BQ * BQ;
   const int q_end = min(N, min(k0 + BK, N) + wl);
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void bwd_simple_kernel(const T* __restric
         }
         float dtanh = 1.f;
         if (SOFTCAP) {
-          const float th = tanh_f32(s / softcap);
+          const float th = tanh_scaled(s, cap_k);
           s = softcap * th;
           dtanh = 1.f - th * th;
         }
@@ -205,27 +208,31 @@ __global__ __launch_bounds__(kThreads) void bwd_simple_kernel(const T* __restric
         sdS[r][c] = p * (dp * zd - sD[r]) * dtanh;
       }
       __syncthreads();
-      // dV += P^T dO and dK += dS^T Q for key r (this thread's key row).
-#pragma unroll
-      for (int k = 0; k < DX; ++k) {
-        const int x = sub + 8 * k;
-        float av = acc_dv[k], ak = acc_dk[k];
-        for (int rr = 0; rr < BQ; ++rr) {
-          av = fmaf(sP[rr][r], sdO[rr][x], av);
-          ak = fmaf(sdS[rr][r], sQ[rr][x], ak);
-        }
-        acc_dv[k] = av;
-        acc_dk[k] = ak;
-      }
-      // dQ partial of this (query block, key block) pair, unscaled.
-      if (ATOMIC_DQ && row < N) {
+      // dV += P^T dO and dK += dS^T Q for key r (this thread's key row),
+      // query rows outer.
+#pragma unroll 2
+      for (int rr = 0; rr < BQ; ++rr) {
+        const float pv = sP[rr][r], dsv = sdS[rr][r];
 #pragma unroll
         for (int k = 0; k < DX; ++k) {
-          const int x = sub + 8 * k;
-          float a = 0.f;
-          for (int c = 0; c < BK; ++c) a = fmaf(sdS[r][c], sK[c][x], a);
-          atomic_add_f32(dQacc + (q_off + row) * D + x, a);
+          acc_dv[k] = fmaf(pv, sdO[rr][sub + 8 * k], acc_dv[k]);
+          acc_dk[k] = fmaf(dsv, sQ[rr][sub + 8 * k], acc_dk[k]);
         }
+      }
+      // dQ partial of this (query block, key block) pair, unscaled: keys
+      // outer, so only this lane's DX partial sums are live.
+      if (ATOMIC_DQ && row < N) {
+        float a[DX];
+#pragma unroll
+        for (int k = 0; k < DX; ++k) a[k] = 0.f;
+#pragma unroll 4
+        for (int c = 0; c < BK; ++c) {
+          const float ds = sdS[r][c];
+#pragma unroll
+          for (int k = 0; k < DX; ++k) a[k] = fmaf(ds, sK[c][sub + 8 * k], a[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < DX; ++k) atomic_add_f32(dQacc + (q_off + row) * D + sub + 8 * k, a[k]);
       }
     }
   }
@@ -275,6 +282,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_simple_kernel(
   const float lse2 = row < N ? LSE[q_off + row] * kLog2e : INFINITY;
   const float dval = row < N ? Dv[q_off + row] : 0.f;
   const float zscale = scale * kLog2e;
+  const float cap_k = SOFTCAP ? 2.f * kLog2e / softcap : 0.f;  // tanh(x / c) = tanh_scaled(x, cap_k)
   float acc[DX];
 #pragma unroll
   for (int k = 0; k < DX; ++k) acc[k] = 0.f;
@@ -301,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_simple_kernel(
       }
       float dtanh = 1.f;
       if (SOFTCAP) {
-        const float th = tanh_f32(s / softcap);
+        const float th = tanh_scaled(s, cap_k);
         s = softcap * th;
         dtanh = 1.f - th * th;
       }
@@ -312,12 +320,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_simple_kernel(
       sdS[r][c] = p * (dp * zd - dval) * dtanh;
     }
     __syncthreads();
+#pragma unroll 2
+    for (int c = 0; c < BK; ++c) {
+      const float dsv = sdS[r][c];
 #pragma unroll
-    for (int k = 0; k < DX; ++k) {
-      const int x = sub + 8 * k;
-      float a = acc[k];
-      for (int c = 0; c < BK; ++c) a = fmaf(sdS[r][c], sK[c][x], a);
-      acc[k] = a;
+      for (int k = 0; k < DX; ++k) acc[k] = fmaf(dsv, sK[c][sub + 8 * k], acc[k]);
     }
   }
   if (row < N) {
