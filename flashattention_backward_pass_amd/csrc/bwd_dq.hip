@@ -21,10 +21,12 @@
 //   dQ  += dS K       (dS^T accumulator layout = A operand with queries on
 //                      lanes; K^T read transposed from the row-major K tile)
 // Computing S^T rather than S puts one query per lane, so LSE and D are one
-// register each.
+// register each.  Wave priorities: S/dP chain 0, softmax 2, dQ chain 1.
 // Dropout (FlashAttention-v1 page, eq (12)): dP^T is multiplied by the
 // replayed mask Z before dS; the quad of lanes holding 4 consecutive queries
 // evaluates the 8 generator calls of a 32-key half together (philox.h).
+#include <type_traits>
+
 #include "fabwd_launch.h"
 #include "mfma_common.h"
 
@@ -46,8 +48,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     Dropout drop) {
   constexpr int KC = D / 16;
   constexpr int NT = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BK * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][BK * D];
+  // Double buffers as separate variables: the compiler gives each LDS
+  // variable its own alias scope, so reads of one buffer do not wait for the
+  // asynchronous copies still landing in the other.
+  __shared__ __attribute__((aligned(1024))) uint16_t sK0[BK * D], sK1[BK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV0[BK * D], sV1[BK * D];
+  auto bufsel = [](auto bufc, auto* a0, auto* a1) {
+    if constexpr (decltype(bufc)::value == 0) return a0;
+    else return a1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -103,7 +112,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Copy key/value block `step` into LDS buffer step%2 with buffer loads that
   // write LDS directly (scalar base per block; a ragged block clamps its rows
   // to the last valid key).
-  auto issue = [&](int step) {
+  auto issue = [&](auto bufc, int step) {
     const int kb = step * BK;
     const int rows = min(BK, N - kb);
     const __amdgpu_buffer_rsrc_t rk =
@@ -117,18 +126,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int row = min((s * 4 + w) * RPS + lane / (D / 8), rows - 1);
         voff = (row * D + 8 * ((lane % (D / 8)) ^ swz<D>((s * 4 + w) * RPS + lane / (D / 8)))) * 2;
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)&sK[step & 1][(s * 4 + w) * 512], 16, voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&sV[step & 1][(s * 4 + w) * 512], 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)&bufsel(bufc, sK0, sK1)[(s * 4 + w) * 512], 16, voff,
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&bufsel(bufc, sV0, sV1)[(s * 4 + w) * 512], 16, voff,
+                                               0, 0, 0);
     }
   };
 
-  if (s_lo < s_hi) issue(s_lo);
-  for (int step = s_lo; step < s_hi; ++step) {
-    const int buf = step & 1;
+  // One key block in buffer BUF (the loop below alternates the buffers with
+  // compile-time selection, so every LDS access names one variable).
+  auto body = [&](auto bufc, int step) __attribute__((always_inline)) {
+    using NB = std::integral_constant<int, 1 - decltype(bufc)::value>;
+    const uint16_t* sk = bufsel(bufc, sK0, sK1);
+    const uint16_t* sv = bufsel(bufc, sV0, sV1);
     const int kb = step * BK;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // block `step` in LDS; buffer (step+1)%2 no longer read
-    if (step + 1 < s_hi) issue(step + 1);
+    __syncthreads();  // block `step` in this buffer; the other buffer no longer read
+    if (step + 1 < s_hi) issue(NB{}, step + 1);
     // Unmasked: every key of the block is visible to every row of this block.
     const bool masked = kb + BK > N || kb < q_hi - wl || kb + BK - 1 > q0 + wr;
 #pragma unroll
@@ -136,12 +150,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       // S^T, dP^T for keys kb + 32 s .. + 31 (rows) x this wave's 32 queries (columns).
       f32x16_t st = {}, dpt = {};
       const int row = 32 * s + l32;
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
         const int off = swz_off<D>(row, 2 * c + g, 0);
-        st = mfma32(*reinterpret_cast<const bf16x8_t*>(&sK[buf][off]), qreg[c], st);
-        dpt = mfma32(*reinterpret_cast<const bf16x8_t*>(&sV[buf][off]), doreg[c], dpt);
+        st = mfma32(*reinterpret_cast<const bf16x8_t*>(&sk[off]), qreg[c], st);
+        dpt = mfma32(*reinterpret_cast<const bf16x8_t*>(&sv[off]), doreg[c], dpt);
       }
+      // The two waves of a SIMD overlap one's softmax with the other's matrix
+      // instructions; the softmax phase (mask generator included) issues at
+      // the higher priority so it finishes while the matrix core is busy.
+      __builtin_amdgcn_s_setprio(2);
       DropBits keep;
       if (DROPOUT) {
         DropQueryLane gen;
@@ -174,6 +193,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       bf16x8_t dsf[2];
       dsf[0] = pack_bf16x8(st, 0);
       dsf[1] = pack_bf16x8(st, 8);
+      __builtin_amdgcn_s_setprio(1);
       // dQ += dS K over these 32 keys: K operand rows 32 s + 16u + 4g + (0..3) and +8.
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
@@ -182,12 +202,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int r0 = 32 * s + 16 * u + 4 * g + (j16 >> 2);
-          const bf16x8_t kop = cat8(lds_read_tr(&sK[buf][swz_off<D>(r0, ch, sub)]),
-                                    lds_read_tr(&sK[buf][swz_off<D>(r0 + 8, ch, sub)]));
+          const bf16x8_t kop = cat8(lds_read_tr(&sk[swz_off<D>(r0, ch, sub)]),
+                                    lds_read_tr(&sk[swz_off<D>(r0 + 8, ch, sub)]));
           dq_acc[n] = mfma32(dsf[u], kop, dq_acc[n]);
         }
       }
     }
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  if (s_lo < s_hi) issue(B0{}, s_lo);
+  for (int step = s_lo; step < s_hi; step += 2) {
+    body(B0{}, step);
+    if (step + 1 < s_hi) body(B1{}, step + 1);
   }
 
   // dQaccum rows of this wave (unscaled).  Register r: row 32w + 8(r/4) + 4g + r%4.

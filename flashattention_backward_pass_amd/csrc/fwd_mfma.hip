@@ -156,11 +156,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         st[r] = (key < N && key <= my_q + wr && key >= my_q - wl) ? 0.f : -__builtin_inff();
       }
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int c = 0; c < KC; ++c)
       st = mfma32(*reinterpret_cast<const bf16x8_t*>(&sk[off_a[c] + 32 * s * D]), qreg[c], st);
     // Phases (S chain | softmax | O chain) stay in order: bounded live ranges.
     __builtin_amdgcn_sched_barrier(0);
+    // The softmax phase issues at a higher priority than the matrix chains,
+    // so it completes under the other wave's matrix instructions.
+    __builtin_amdgcn_s_setprio(2);
     // Mask bits of this half (the other wave's matrix instructions overlap).
     DropBits keep;
     if (DROPOUT) {
@@ -215,6 +219,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       pf[u] = __builtin_bit_cast(bf16x8_t, pw);
     }
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
     // O^T += V^T P^T: k = keys 32s + 16u + (accumulator row order), d on lanes.
 #pragma unroll
     for (int n = 0; n < NT; ++n)
