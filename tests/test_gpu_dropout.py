@@ -30,6 +30,10 @@ CASES = [
     (1, 8, 2, 512, 128, "bf16", True, 0.0, (-1, -1), 0.15),  # grouped heads (head split)
     (1, 2, 1, 333, 64, "bf16", True, 0.0, (50, -1), 0.25),    # causal window, ragged
     (1, 2, 2, 256, 128, "bf16", False, 0.0, (-1, -1), 0.9),
+    (1, 1, 1, 1, 128, "bf16", True, 0.0, (-1, -1), 0.5),      # one key
+    (1, 4, 1, 5, 64, "bf16", False, 3.0, (2, 1), 0.3),        # tiny: every mask and the cap
+    (2, 8, 2, 200, 64, "bf16", True, 10.0, (60, -1), 0.2),    # GQA d=64, cap, window
+    (1, 2, 2, 64, 64, "fp32", True, 0.0, (-1, -1), 0.999),    # almost everything dropped
 ]
 
 
