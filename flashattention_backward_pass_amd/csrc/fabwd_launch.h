@@ -40,7 +40,10 @@ hipError_t launch_bwd(const Problem& p, const void* Q, const void* K, const void
                       const float* LSE, const float* D, float* dQacc, void* dK, void* dV, hipStream_t s);
 hipError_t launch_bwd_dq_convert(const Problem& p, const float* dQacc, void* dQ, hipStream_t s);
 
-// Kernel families behind launch_fwd_stats / launch_bwd (dispatch.cpp picks one).
+// Kernel families behind launch_fwd_stats / launch_bwd (dispatch.cpp picks
+// one): the *_simple launchers are the fp32 vector kernels (fp32 only; they
+// return hipErrorInvalidValue for bf16), the *_mfma launchers the bf16
+// matrix-core kernels.
 hipError_t launch_fwd_simple(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,
                              hipStream_t s);
 hipError_t launch_fwd_mfma(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,

@@ -1,6 +1,5 @@
 // Building blocks shared by the gfx950 matrix-core kernels: the bf16 MFMA,
-// the transposing LDS read, the row swizzle of bf16 tiles in LDS and the
-// asynchronous global -> LDS copies.
+// the transposing LDS read and the row swizzle of bf16 tiles in LDS.
 #pragma once
 
 #include "fabwd_device.h"
@@ -8,7 +7,6 @@
 namespace fabwd {
 
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
-typedef __attribute__((address_space(1))) void global_void_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // D (32x32 fp32) += A (32x16 bf16) * B (16x32 bf16).
@@ -65,34 +63,6 @@ __device__ __forceinline__ int swz(int row) {
 template <int D>
 __device__ __forceinline__ int swz_off(int row, int chunk, int sub) {
   return row * D + 8 * (chunk ^ swz<D>(row)) + sub;
-}
-
-// Asynchronous copy global -> LDS (global_load_lds): the 64 lanes of the wave
-// fill 64 * bytes of LDS starting at the wave-uniform `lds_base`, lane L at
-// lds_base + bytes * L, each lane reading its own global address.  Completion
-// is tracked by vmcnt.
-__device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((global_void_t*)(gsrc), (lds_void_t*)(lds_base), 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((global_void_t*)(gsrc), (lds_void_t*)(lds_base), 4, 0, 0);
-}
-
-// Copies `rows` rows (multiple of 1024 / (2 D)) of a row-major bf16 matrix into
-// a swizzled LDS tile with the 4 waves of a 256-thread workgroup.  Source rows
-// at or past `n_valid` read row n_valid - 1 instead (always in bounds).
-template <int D, int ROWS>
-__device__ __forceinline__ void dma_tile(const bf16_t* src_row0, int n_valid, uint16_t* tile, int lane, int w) {
-  constexpr int kRowsPerSlab = 1024 / (2 * D);
-  constexpr int kSlabs = ROWS / kRowsPerSlab;
-  static_assert(kSlabs % 4 == 0, "tile must split evenly over 4 waves");
-#pragma unroll
-  for (int s = 0; s < kSlabs / 4; ++s) {
-    const int I = s * 4 + w;
-    const int row = I * kRowsPerSlab + lane / (D / 8);
-    const int chunk = (lane % (D / 8)) ^ swz<D>(row);
-    dma16(src_row0 + int64_t(min(row, n_valid - 1)) * D + 8 * chunk, tile + I * 512);
-  }
 }
 
 }  // namespace fabwd

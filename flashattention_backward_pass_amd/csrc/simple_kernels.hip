@@ -1,8 +1,7 @@
 // Vector-ALU (fp32 FMA) forward and backward kernels.
 //
 // These serve the fp32 workloads (on MI355X the fp32 vector and fp32 matrix
-// peaks are the same, 157.3 TFLOP/s) and any configuration the bf16 MFMA
-// kernels do not cover.  They follow the tiling of
+// peaks are the same, 157.3 TFLOP/s); bf16 runs on the matrix-core kernels.  They follow the tiling of
 // "解析 FlashAttention（3）：FlashAttention-v1 反向传播", section 4 (Algorithm 4):
 // key/value blocks outer, query blocks inner, P recomputed per tile from the
 // saved LSE (Inference Cookbook "反向传播算法详解", section 1.2), dK and dV kept
@@ -389,18 +388,14 @@ hipError_t bwd_dq_simple_d(const Problem& p, const void* Q, const void* K, const
 
 hipError_t launch_fwd_simple(const Problem& p, const void* Q, const void* K, const void* V, void* O, float* LSE,
                              hipStream_t s) {
-  if (p.dtype == 1)
-    return p.d == 64 ? fwd_simple_d<bf16_t, 64>(p, Q, K, V, O, LSE, s)
-                     : fwd_simple_d<bf16_t, 128>(p, Q, K, V, O, LSE, s);
+  if (p.dtype != 0) return hipErrorInvalidValue;
   return p.d == 64 ? fwd_simple_d<float, 64>(p, Q, K, V, O, LSE, s)
                    : fwd_simple_d<float, 128>(p, Q, K, V, O, LSE, s);
 }
 
 hipError_t launch_bwd_simple(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                              const float* LSE, const float* Dv, float* dQacc, void* dK, void* dV, hipStream_t s) {
-  if (p.dtype == 1)
-    return p.d == 64 ? bwd_simple_d<bf16_t, 64>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s)
-                     : bwd_simple_d<bf16_t, 128>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s);
+  if (p.dtype != 0) return hipErrorInvalidValue;
   return p.d == 64 ? bwd_simple_d<float, 64>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s)
                    : bwd_simple_d<float, 128>(p, Q, K, V, dO, LSE, Dv, dQacc, dK, dV, s);
 }
@@ -411,9 +406,7 @@ namespace fabwd {
 
 hipError_t launch_bwd_dq_simple(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                                 const float* LSE, const float* Dv, float* dQacc, hipStream_t s) {
-  if (p.dtype == 1)
-    return p.d == 64 ? bwd_dq_simple_d<bf16_t, 64>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
-                     : bwd_dq_simple_d<bf16_t, 128>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
+  if (p.dtype != 0) return hipErrorInvalidValue;
   return p.d == 64 ? bwd_dq_simple_d<float, 64>(p, Q, K, V, dO, LSE, Dv, dQacc, s)
                    : bwd_dq_simple_d<float, 128>(p, Q, K, V, dO, LSE, Dv, dQacc, s);
 }
