@@ -60,11 +60,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int l32 = lane & 31, g = lane >> 5;
   const int j16 = lane & 15, h16 = (lane >> 4) & 1;
 
+  // Work unit: the key/value head varies fastest, so that with the
+  // round-robin placement of workgroups on the 8 XCDs the query heads of one
+  // group share an XCD (and its L2 holds their K, V); then the query head in
+  // the group; query blocks vary slowest, last (heaviest under a causal
+  // mask) first.
   const int n_qblk = (N + BQ - 1) / BQ;
-  const int bhq = blockIdx.x % BHq;
-  const int iblk = n_qblk - 1 - int(blockIdx.x / BHq);  // heaviest causal blocks first
-  const int b = bhq / H, h = bhq % H;
-  const int hk = h / (H / H_kv);
+  const int G = H / H_kv;
+  const int BHkv = BHq / G;
+  const int kvu = int(blockIdx.x % unsigned(BHkv));
+  const int rest = int(blockIdx.x / unsigned(BHkv));
+  const int b = kvu / H_kv, hk = kvu % H_kv;
+  const int h = hk * G + rest % G;
+  const int bhq = b * H + h;
+  const int iblk = n_qblk - 1 - rest / G;
   const int q0 = iblk * BQ;
   const int64_t q_off = (int64_t(b) * H + h) * N;
   const int64_t kv_off = (int64_t(b) * H_kv + hk) * N;
