@@ -1,0 +1,69 @@
+"""The backward step (preprocess, bwd, dq_convert) captured in a HIP graph.
+
+The library only enqueues kernels on the caller's stream (no memsets, no
+allocations, no synchronisation), so a captured step must replay to the
+bitwise result of the eager calls.  Each replay is checked, with eager work
+and synchronisations of the program in between, for the bf16 matrix-core
+path (with dropout and a head split as well) and the fp32 path.
+"""
+import pytest
+import torch
+
+import flashattention_backward_pass_amd as fab
+from flashattention_backward_pass_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # B, H, H_kv, N, d, dtype, causal, dropout, deterministic
+    (1, 4, 4, 512, 128, "bf16", True, None, False),
+    (1, 8, 2, 384, 128, "bf16", True, (0.2, 1234, 5), False),  # grouped heads: head split through dQaccum
+    (2, 2, 2, 200, 64, "fp32", False, None, True),              # fp32, fixed summation order
+    (2, 2, 2, 200, 64, "fp32", True, None, False),              # fp32, dQ by atomics into the zeroed dQaccum
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["bf16", "bf16_gqa_dropout", "fp32_det", "fp32_atomic"])
+def test_graph_replays_match_eager(case):
+    B, H, Hkv, N, d, dt, causal, drop, det = case
+    w = workloads.custom(B, H, Hkv, N, d, dt, causal, 0.0, seed=N + H, name="graph", dropout=drop)
+    x = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x[n].to(dev) for n in ("Q", "K", "V", "dO"))
+    kw = dict(causal=causal, scale=w.tau, dropout=drop)
+    o, lse = fab.attention_forward(q, k, v, **kw)
+    D = torch.empty(B, H, N, device=dev)
+    acc = torch.empty(B, H, N, d, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step():
+        fab.attn_bwd_preprocess(o, do, D, acc, H_kv=Hkv, causal=causal, scale=w.tau)
+        fab.attn_bwd(q, k, v, do, lse, D, acc, dk, dv, deterministic=det, **kw)
+        fab.attn_bwd_dq_convert(acc, dq, scale=w.tau)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (D, dq, dk, dv)]
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in (D, dq, dk, dv, acc):
+            t.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("D", "dQ", "dK", "dV"), (D, dq, dk, dv), ref):
+            if dt == "fp32" and not det and name == "dQ":
+                # atomic summation order is free: equal up to fp32 rounding
+                err = float((a - b).abs().max() / b.abs().max())
+                assert err <= 1e-5, f"replay {rep}: dQ differs by {err:.2e}"
+            else:
+                assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager result"
