@@ -182,19 +182,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       gen.rounds(0, 10);
       keep = gen.finish(lane);
     }
-    // Scores in log2 units; new max over these keys and the partner lane's.
+    // New max (log2 units) over these keys and the partner lane's.  With a
+    // cap, st becomes the capped score in log2 units; without one st stays
+    // the raw score (tau > 0 keeps the order), the max is scaled once, and
+    // the scale folds into the exponent below.
     float mx = -__builtin_inff();
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float z = st[r];
-      // The cap would turn a masked -inf into a finite -c: keep it -inf.
-      if (SOFTCAP)
-        z = (MASKED && z == -__builtin_inff()) ? z : cap_zs * tanh_scaled(z, cap_k);
-      else
-        z *= zs;  // -inf stays -inf
-      st[r] = z;
-      mx = fmaxf(mx, z);
+      if (SOFTCAP) {
+        // The cap would turn a masked -inf into a finite -c: keep it -inf.
+        const float z = (MASKED && st[r] == -__builtin_inff()) ? st[r] : cap_zs * tanh_scaled(st[r], cap_k);
+        st[r] = z;
+      }
+      mx = fmaxf(mx, st[r]);
     }
+    if (!SOFTCAP) mx *= zs;  // -inf stays -inf
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     // Lazy rescale: raise m only when a score exceeds it by more than kLazy.
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
@@ -216,8 +218,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       u32x4_t pw;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float p0 = fast_exp2(st[8 * u + 2 * k] - mu);
-        const float p1 = fast_exp2(st[8 * u + 2 * k + 1] - mu);
+        const float p0 = fast_exp2(SOFTCAP ? st[8 * u + 2 * k] - mu : fmaf(st[8 * u + 2 * k], zs, -mu));
+        const float p1 = fast_exp2(SOFTCAP ? st[8 * u + 2 * k + 1] - mu : fmaf(st[8 * u + 2 * k + 1], zs, -mu));
         l += p0 + p1;
         if (DROPOUT)
           pw[k] = pack_bf16x2(keep.keep(8 * u + 2 * k, drop.keep_t) ? p0 : 0.f,
