@@ -10,7 +10,10 @@
 
 namespace {
 
-constexpr int64_t kMaxElems = int64_t(1) << 40;
+// 2^36 elements (above any problem that fits in device memory) keeps every
+// grid within the 32-bit work-item count of a dispatch: the largest grid has
+// about 2 B*H*N <= 2^31 work-items for d >= 64.
+constexpr int64_t kMaxElems = int64_t(1) << 36;
 constexpr int kMaxN = 1 << 24;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -52,7 +52,7 @@
  *    attn_fwd_stats and attn_bwd; callers advance rng_offset (or the seed)
  *    between layers and steps.
  *  - Every pointer must be 16-byte aligned.  Sizes with B*H*N*d beyond
- *    2^40 elements are rejected.  N = 0 or B = 0 is a valid empty problem:
+ *    2^36 elements (more than device memory holds) are rejected.  N = 0 or B = 0 is a valid empty problem:
  *    the call validates its arguments and enqueues nothing.
  *  - Return value: ATTN_OK (0) or one of the ATTN_ERR_* codes below.  On an
  *    error nothing is enqueued.  No exception crosses this interface.

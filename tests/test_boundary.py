@@ -132,6 +132,13 @@ def test_misaligned_pointers(lib):
 
 def test_too_many_elements(lib):
     assert call_all(lib, fab.make_params(1 << 12, 1 << 10, 1, 1 << 13, 128, 1)) == [fab.ATTN_ERR_INVALID_ARG] * 4
+    # B*H*N*d just above 2^36 is rejected; exactly 2^36 passes the size check, so
+    # those calls fail on the (null or misaligned) pointers instead.
+    over = fab.make_params(1, 1 << 9, 1 << 9, (1 << 20) + 1, 128, 1)
+    assert call_all(lib, over) == [fab.ATTN_ERR_INVALID_ARG] * 4
+    at = fab.make_params(1, 1 << 9, 1 << 9, 1 << 20, 128, 1)
+    assert call_all(lib, at, ptr=ctypes.c_void_p(0)) == [fab.ATTN_ERR_INVALID_ARG] * 4  # null pointers
+    assert call_all(lib, at, ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * 4  # size accepted, pointer checked next
 
 
 @pytest.mark.parametrize("shape", [(0, 2, 2, 64), (1, 2, 2, 0)])
