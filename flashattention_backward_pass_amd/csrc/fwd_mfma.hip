@@ -176,12 +176,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __builtin_amdgcn_s_setprio(2);
     // Mask bits of this half (the other wave's matrix instructions overlap).
     DropBits keep;
-    if (DROPOUT) {
-      DropQueryLane gen;
-      gen.init(drop, uint32_t(bhq), kb + 32 * s, my_q, lane);
-      gen.rounds(0, 10);
-      keep = gen.finish(lane);
-    }
+    if (DROPOUT) keep = DropQueryLane::sequential(drop, uint32_t(bhq), kb + 32 * s, my_q, lane);
     // New max (log2 units) over these keys and the partner lane's.  With a
     // cap, st becomes the capped score in log2 units; without one st stays
     // the raw score (tau > 0 keeps the order), the max is scaled once, and

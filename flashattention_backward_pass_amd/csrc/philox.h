@@ -170,30 +170,51 @@ struct DropQueryLane {
       c[1].round();
     }
   }
-  __device__ __forceinline__ DropBits finish(int lane) const {
+  // 4x4 transpose of words across the quad: a[i] = word i of this lane's
+  // call (run lane&3) becomes a[m] = word (lane&3) of run m's call.
+  static __device__ __forceinline__ void quad_transpose(uint32_t (&a)[4], int lane) {
     const bool b0 = lane & 1, b1 = lane & 2;
+    // Stage 1: swap 2x2 blocks across lanes l ^ 2.
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t r = swap_lane2(b1 ? a[i] : a[i + 2]);
+      a[i] = b1 ? r : a[i];
+      a[i + 2] = b1 ? a[i + 2] : r;
+    }
+    // Stage 2: swap elements across lanes l ^ 1.
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+      const uint32_t r = swap_lane1(b0 ? a[i] : a[i + 1]);
+      a[i] = b0 ? r : a[i];
+      a[i + 1] = b0 ? a[i + 1] : r;
+    }
+  }
+  __device__ __forceinline__ DropBits finish(int lane) const {
     DropBits out;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      // a[i] = word i of this lane's call (run lane&3, pair j); after the
-      // transpose a[m] = word (lane&3) of run m's call, pair j.
       uint32_t a[4] = {c[j].x0, c[j].x1, c[j].x2, c[j].x3};
-      // Stage 1: swap 2x2 blocks across lanes l ^ 2.
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint32_t r = swap_lane2(b1 ? a[i] : a[i + 2]);
-        a[i] = b1 ? r : a[i];
-        a[i + 2] = b1 ? a[i + 2] : r;
-      }
-      // Stage 2: swap elements across lanes l ^ 1.
-#pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        const uint32_t r = swap_lane1(b0 ? a[i] : a[i + 1]);
-        a[i] = b0 ? r : a[i];
-        a[i + 1] = b0 ? a[i + 1] : r;
-      }
+      quad_transpose(a, lane);
 #pragma unroll
       for (int m = 0; m < 4; ++m) out.w[2 * m + j] = a[m];
+    }
+    return out;
+  }
+  // The same bits as init + rounds(0, 10) + finish, one call at a time: one
+  // generator state live instead of two.
+  static __device__ __forceinline__ DropBits sequential(const Dropout& d, uint32_t bh, int k_row0, int q, int lane) {
+    const int m = lane & 3, g = (lane >> 5) & 1;
+    const int k = k_row0 + 8 * m + 4 * g;
+    DropBits out;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      PhiloxState s;
+      s.init((uint32_t(k) >> 1) + uint32_t(j), uint32_t(q) >> 2, bh, d.offset, d);
+      s.rounds(0, 10);
+      uint32_t a[4] = {s.x0, s.x1, s.x2, s.x3};
+      quad_transpose(a, lane);
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) out.w[2 * mm + j] = a[mm];
     }
     return out;
   }
