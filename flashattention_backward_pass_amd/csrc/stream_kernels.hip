@@ -37,37 +37,50 @@ __device__ __forceinline__ void load16<bf16_t>(const bf16_t* p, float* out) {
   }
 }
 
-// One lane handles 16 bytes of a row of O and dO.  Grid-stride over row groups.
+// One lane handles 16 bytes of a row of O and dO, for kUnroll row groups at a
+// time (all loads issued before any arithmetic, so more bytes are in flight).
+// Grid-stride over row groups.
+constexpr int kUnroll = 4;
+
 template <typename T, int D, bool ZERO_ACC>
 __global__ __launch_bounds__(kThreads) void preprocess_kernel(const T* __restrict__ O, const T* __restrict__ dO,
                                                               float* __restrict__ Dout,
                                                               float* __restrict__ dQacc, int64_t rows) {
   constexpr int kPerLane = 16 / sizeof(T);      // elements per 16-byte access
   constexpr int L = D / kPerLane;                // lanes per row
-  constexpr int kRowsPerBlock = kThreads / L;
+  constexpr int kRowsPerGroup = kThreads / L;    // rows covered by the block at once
   constexpr int kZeroPerLane = (D / 4) / L;      // float4 zero stores per lane
   static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "row must map to a power-of-two lane group");
   const int lane_in_row = threadIdx.x % L;
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t row0 = int64_t(blockIdx.x) * kRowsPerBlock; row0 < rows;
-       row0 += int64_t(gridDim.x) * kRowsPerBlock) {
-    const int64_t row = row0 + threadIdx.x / L;
-    float acc = 0.f;
-    if (row < rows) {
-      const int64_t off = row * D + int64_t(lane_in_row) * kPerLane;
-      float o[kPerLane], g[kPerLane];
-      load16<T>(O + off, o);
-      load16<T>(dO + off, g);
+  for (int64_t row0 = int64_t(blockIdx.x) * kRowsPerGroup * kUnroll; row0 < rows;
+       row0 += int64_t(gridDim.x) * kRowsPerGroup * kUnroll) {
+    u32x4_t ob[kUnroll], gb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t row = row0 + u * kRowsPerGroup + threadIdx.x / L;
+      const int64_t off = min(row, rows - 1) * D + int64_t(lane_in_row) * kPerLane;
+      ob[u] = *reinterpret_cast<const u32x4_t*>(O + off);
+      gb[u] = *reinterpret_cast<const u32x4_t*>(dO + off);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t row = row0 + u * kRowsPerGroup + threadIdx.x / L;
+      float o[kPerLane], g[kPerLane], acc = 0.f;
+      load16<T>(reinterpret_cast<const T*>(&ob[u]), o);
+      load16<T>(reinterpret_cast<const T*>(&gb[u]), g);
 #pragma unroll
       for (int e = 0; e < kPerLane; ++e) acc = fmaf(o[e], g[e], acc);
-      if (ZERO_ACC) {
-        f32x4_t* z = reinterpret_cast<f32x4_t*>(dQacc + row * D) + lane_in_row * kZeroPerLane;
+      acc = wave_xor_sum(acc, L);
+      if (row < rows) {
+        if (lane_in_row == 0) Dout[row] = acc;
+        if (ZERO_ACC) {
+          f32x4_t* z = reinterpret_cast<f32x4_t*>(dQacc + row * D) + lane_in_row * kZeroPerLane;
 #pragma unroll
-        for (int e = 0; e < kZeroPerLane; ++e) z[e] = zero;
+          for (int e = 0; e < kZeroPerLane; ++e) z[e] = zero;
+        }
       }
     }
-    acc = wave_xor_sum(acc, L);
-    if (row < rows && lane_in_row == 0) Dout[row] = acc;
   }
 }
 
@@ -122,7 +135,8 @@ hipError_t preprocess_t(const Problem& p, const void* O, const void* dO, float* 
   constexpr int L = D / (16 / sizeof(T));
   const int64_t rows = p.q_rows();
   constexpr bool kZero = sizeof(T) == 4;  // only the fp32 backward accumulates into dQaccum
-  hipLaunchKernelGGL((preprocess_kernel<T, D, kZero>), dim3(grid_for(rows, kThreads / L)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((preprocess_kernel<T, D, kZero>), dim3(grid_for(rows, kThreads / L * kUnroll)), dim3(kThreads),
+                     0, s,
                      static_cast<const T*>(O), static_cast<const T*>(dO), Dv, dQacc, rows);
   return hipGetLastError();
 }
