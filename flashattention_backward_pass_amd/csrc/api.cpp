@@ -10,11 +10,16 @@
 
 namespace {
 
-// 2^36 elements (above any problem that fits in device memory) keeps every
-// grid within the 32-bit work-item count of a dispatch: the largest grid has
-// about 2 B*H*N <= 2^31 work-items for d >= 64.
+// 2^36 elements per tensor is more than device memory holds.
 constexpr int64_t kMaxElems = int64_t(1) << 36;
 constexpr int kMaxN = 1 << 24;
+// A dispatch counts its work-items in 32 bits.  The matrix-core kernels launch
+// at most 2 * B * H * ceil(N / 128) workgroups of 256 work-items (2: the
+// grouped-head split of the dK/dV kernel), so short sequences with very many
+// heads are the case this bounds.  The fp32 kernels put H (or H_kv) and B in
+// the second and third grid dimensions, each at most 65535 blocks.
+constexpr int64_t kMaxWorkItems = (int64_t(1) << 32) - 1;
+constexpr int kMaxGridYZ = 65535;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -35,6 +40,9 @@ int check_params(const attn_params* p, fabwd::Problem* out, bool* empty) {
   if (p->N > kMaxN) return ATTN_ERR_INVALID_ARG;
   const int64_t elems = int64_t(p->B) * p->H * p->N * p->d;
   if (elems > kMaxElems) return ATTN_ERR_INVALID_ARG;
+  const int64_t max_blocks = 2 * int64_t(p->B) * p->H * ((int64_t(p->N) + 127) / 128);
+  if (max_blocks * 256 > kMaxWorkItems) return ATTN_ERR_INVALID_ARG;
+  if (p->dtype == ATTN_FP32 && (p->B > kMaxGridYZ || p->H > kMaxGridYZ)) return ATTN_ERR_INVALID_ARG;
   out->B = p->B;
   out->H = p->H;
   out->H_kv = p->H_kv;

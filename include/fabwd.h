@@ -51,9 +51,13 @@
  *    undropped P.  The same (seed, offset, dropout_p) must be passed to
  *    attn_fwd_stats and attn_bwd; callers advance rng_offset (or the seed)
  *    between layers and steps.
- *  - Every pointer must be 16-byte aligned.  Sizes with B*H*N*d beyond
- *    2^36 elements (more than device memory holds) are rejected.  N = 0 or B = 0 is a valid empty problem:
- *    the call validates its arguments and enqueues nothing.
+ *  - Every pointer must be 16-byte aligned.  Sizes are rejected
+ *    (ATTN_ERR_INVALID_ARG) when B*H*N*d exceeds 2^36 elements (more than
+ *    device memory holds), when N exceeds 2^24, when 2*B*H*ceil(N/128)*256
+ *    reaches 2^32 (a kernel grid would exceed the work-item count of one
+ *    dispatch: very many heads of short sequences), or, for fp32, when B or
+ *    H exceeds 65535.  N = 0 or B = 0 is a valid empty problem: the call
+ *    validates its arguments and enqueues nothing.
  *  - Return value: ATTN_OK (0) or one of the ATTN_ERR_* codes below.  On an
  *    error nothing is enqueued.  No exception crosses this interface.
  */

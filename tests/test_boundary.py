@@ -141,6 +141,19 @@ def test_too_many_elements(lib):
     assert call_all(lib, at, ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * 4  # size accepted, pointer checked next
 
 
+def test_grid_limits(lib):
+    """Short sequences with very many heads: few elements, but a grid of
+    2*B*H*ceil(N/128) workgroups of 256 work-items past 2^32 is rejected."""
+    many = fab.make_params(1 << 22, 4, 4, 1, 64, 1)  # 2^30 elements, 2^33 work-items
+    assert call_all(lib, many) == [fab.ATTN_ERR_INVALID_ARG] * 4
+    fits = fab.make_params(1 << 20, 4, 4, 1, 64, 1)  # 2^31 work-items: size accepted, pointers checked
+    assert call_all(lib, fits, ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * 4
+    # fp32 puts B and H in the second and third grid dimensions
+    assert call_all(lib, fab.make_params(65536, 1, 1, 16, 64, 0), ptr=MIS) == [fab.ATTN_ERR_INVALID_ARG] * 4
+    assert call_all(lib, fab.make_params(65535, 1, 1, 16, 64, 0), ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * 4
+    assert call_all(lib, fab.make_params(65536, 1, 1, 16, 64, 1), ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * 4
+
+
 @pytest.mark.parametrize("shape", [(0, 2, 2, 64), (1, 2, 2, 0)])
 def test_empty_problems_are_ok_without_pointers(lib, shape):
     B, H, Hkv, N = shape
