@@ -175,7 +175,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         gen.rounds(0, 10);
         keep = gen.finish(lane);
       }
-      // Register r: key kb + 32 s + 8(r/4) + 4g + r%4, query my_q.
+      // Register r: key kb + 32 s + 8(r/4) + 4g + r%4, query my_q.  dS is
+      // computed for every key, then masked keys are set to 0 in one pass
+      // under a single uniform branch (a test inside this loop becomes a
+      // branch per element).  The select discards whatever a masked key
+      // produced, inf or NaN included.
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float dt = 1.f;
@@ -187,15 +191,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         } else {
           p = fast_exp2(fmaf(st[r], zs, nl2));
         }
-        if (masked) {
-          const int key = kb + 32 * s + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= N || key > my_q + wr || key < my_q - wl) p = 0.f;
-        }
         float dp = dpt[r];
         if (DROPOUT) dp = keep.keep(r, drop.keep_t) ? dp * drop.scale : 0.f;
         float ds = p * (dp - dval);
         if (SOFTCAP) ds *= dt;
         st[r] = ds;
+      }
+      if (masked) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + 32 * s + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= N || key > my_q + wr || key < my_q - wl) st[r] = 0.f;
+        }
       }
       bf16x8_t dsf[2];
       dsf[0] = pack_bf16x8(st, 0);
