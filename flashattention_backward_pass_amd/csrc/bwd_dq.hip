@@ -100,6 +100,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
   for (int n = 0; n < NT; ++n) dq_acc[n] = f32x16_t{};
 
+  // LDS element offsets of this lane's operand reads within a K or V block.
+  // The swizzle depends on the row mod 16 only, so rows 32 s + l32 (row
+  // reads) and 32 s + 16 u + 4 g + j16/4 (+ 8) (transposed reads) are these
+  // offsets plus a multiple of 16 D.  The empty asm hides their bits from the
+  // compiler: otherwise it forms the V and second-buffer addresses with a
+  // bitwise or, which an LDS instruction cannot take as its immediate offset,
+  // and keeps a register for every (buffer, tensor, half) variant.
+  int roff[KC], toff[NT][2];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    roff[c] = swz_off<D>(l32, 2 * c + g, 0);
+    asm volatile("" : "+v"(roff[c]));
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int ch = 4 * n + 2 * h16 + ((j16 & 3) >> 1);
+    const int sub = 4 * (j16 & 1);
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      toff[n][v] = swz_off<D>(4 * g + (j16 >> 2) + 8 * v, ch, sub);
+      asm volatile("" : "+v"(toff[n][v]));
+    }
+  }
+
   // Key blocks [s_lo, s_hi) hold every key that some row of this block sees.
   const int q_hi = min(q0 + BQ, N) - 1;  // last valid row
   const int s_lo = max(0, q0 - wl) / BK;
@@ -156,11 +180,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int s = 0; s < 2; ++s) {
       // S^T, dP^T for keys kb + 32 s .. + 31 (rows) x this wave's 32 queries (columns).
       f32x16_t st = {}, dpt = {};
-      const int row = 32 * s + l32;
       __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        const int off = swz_off<D>(row, 2 * c + g, 0);
+        const int off = roff[c] + 32 * s * D;  // row 32 s + l32, chunk 2c + g
         st = mfma32(*reinterpret_cast<const bf16x8_t*>(&sk[off]), qreg[c], st);
         dpt = mfma32(*reinterpret_cast<const bf16x8_t*>(&sv[off]), doreg[c], dpt);
       }
@@ -211,13 +234,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       // dQ += dS K over these 32 keys: K operand rows 32 s + 16u + 4g + (0..3) and +8.
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        const int ch = 4 * n + 2 * h16 + ((j16 & 3) >> 1);
-        const int sub = 4 * (j16 & 1);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int r0 = 32 * s + 16 * u + 4 * g + (j16 >> 2);
-          const bf16x8_t kop = cat8(lds_read_tr(&sk[swz_off<D>(r0, ch, sub)]),
-                                    lds_read_tr(&sk[swz_off<D>(r0 + 8, ch, sub)]));
+          const int rb = (32 * s + 16 * u) * D;
+          const bf16x8_t kop = cat8(lds_read_tr(&sk[toff[n][0] + rb]), lds_read_tr(&sk[toff[n][1] + rb]));
           dq_acc[n] = mfma32(dsf[u], kop, dq_acc[n]);
         }
       }
