@@ -35,6 +35,10 @@ namespace fabwd {
 namespace {
 
 constexpr int kThreads = 256;
+#ifndef FABWD_DQ_PF
+#define FABWD_DQ_PF 2
+#endif
+constexpr int kPF = FABWD_DQ_PF;  // S/dP operand reads in flight ahead of their use
 constexpr int BQ = 128;  // query rows per workgroup
 constexpr int BK = 64;   // keys per inner step
 
@@ -181,11 +185,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       // S^T, dP^T for keys kb + 32 s .. + 31 (rows) x this wave's 32 queries (columns).
       f32x16_t st = {}, dpt = {};
       __builtin_amdgcn_s_setprio(0);
+      // The reads of step c + kPF are issued before the matrix instructions of
+      // step c (the fences keep the scheduler from sinking them to their use).
+      bf16x8_t kop[KC], vop[KC];
+      auto read_ops = [&](int c) {
+        kop[c] = *reinterpret_cast<const bf16x8_t*>(&sk[roff[c] + 32 * s * D]);
+        vop[c] = *reinterpret_cast<const bf16x8_t*>(&sv[roff[c] + 32 * s * D]);
+      };
+#pragma unroll
+      for (int c = 0; c < kPF; ++c) read_ops(c);
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        const int off = roff[c] + 32 * s * D;  // row 32 s + l32, chunk 2c + g
-        st = mfma32(*reinterpret_cast<const bf16x8_t*>(&sk[off]), qreg[c], st);
-        dpt = mfma32(*reinterpret_cast<const bf16x8_t*>(&sv[off]), doreg[c], dpt);
+        if (c + kPF < KC) read_ops(c + kPF);
+        __builtin_amdgcn_sched_barrier(0);
+        st = mfma32(kop[c], qreg[c], st);
+        dpt = mfma32(vop[c], doreg[c], dpt);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // The two waves of a SIMD overlap one's softmax with the other's matrix
       // instructions; the softmax phase (mask generator included) issues at
