@@ -79,9 +79,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   constexpr int NT = D / 32;  // 32-wide column tiles over d
   // Double buffers as separate variables: the compiler gives each LDS
   // variable its own alias scope, so reads of one buffer do not wait for the
-  // asynchronous copies still landing in the other.
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ0[BR * D], sQ1[BR * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sdO0[BR * D], sdO1[BR * D];
+  // asynchronous copies still landing in the other.  Q and dO of one buffer
+  // share a variable (copied and read together): a dO address is then the Q
+  // address plus an immediate offset, not a register of its own.
+  __shared__ __attribute__((aligned(1024))) uint16_t sQO0[2 * BR * D], sQO1[2 * BR * D];
+  uint16_t* const sQ0 = sQO0;
+  uint16_t* const sQ1 = sQO1;
+  uint16_t* const sdO0 = sQO0 + BR * D;
+  uint16_t* const sdO1 = sQO1 + BR * D;
   __shared__ __attribute__((aligned(256))) float sL0[BR], sL1[BR];
   __shared__ __attribute__((aligned(256))) float sD0[BR], sD1[BR];
   __shared__ float sX[4][BR];  // rows rescaled by waves 1-3 in place of the LSE

@@ -35,10 +35,7 @@ namespace fabwd {
 namespace {
 
 constexpr int kThreads = 256;
-#ifndef FABWD_DQ_PF
-#define FABWD_DQ_PF 2
-#endif
-constexpr int kPF = FABWD_DQ_PF;  // S/dP operand reads in flight ahead of their use
+constexpr int kPF = 2;   // S/dP steps whose operand reads run ahead of their use
 constexpr int BQ = 128;  // query rows per workgroup
 constexpr int BK = 64;   // keys per inner step
 
@@ -55,8 +52,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Double buffers as separate variables: the compiler gives each LDS
   // variable its own alias scope, so reads of one buffer do not wait for the
   // asynchronous copies still landing in the other.
-  __shared__ __attribute__((aligned(1024))) uint16_t sK0[BK * D], sK1[BK * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV0[BK * D], sV1[BK * D];
+  // K and V of one buffer share a variable (copied and read together): a V
+  // address is then the K address plus an immediate offset.
+  __shared__ __attribute__((aligned(1024))) uint16_t sKV0[2 * BK * D], sKV1[2 * BK * D];
+  uint16_t* const sK0 = sKV0;
+  uint16_t* const sK1 = sKV1;
+  uint16_t* const sV0 = sKV0 + BK * D;
+  uint16_t* const sV1 = sKV1 + BK * D;
   auto bufsel = [](auto bufc, auto* a0, auto* a1) {
     if constexpr (decltype(bufc)::value == 0) return a0;
     else return a1;
