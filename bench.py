@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="steps timed after evicting the caches (0: skip); reported beside the warm value")
     return ap.parse_args()
 
 
@@ -53,14 +55,15 @@ def source_sha(paths):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(launch_bytes_key="bytes_per_launch"):
+def measured_traffic(workload, launch_bytes_key="bytes_per_launch"):
     """HBM bytes per attn_bwd launch from committed rocprofv3 counter runs,
-    valid only while the kernel source is the one the counters were taken on."""
+    valid only for the workload they were taken on and while the kernel
+    source is the one they were taken on."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != source_sha(BWD_SOURCES):
+    if t.get("workload") != workload or t.get("source_sha") != source_sha(BWD_SOURCES):
         return None
     return t.get(launch_bytes_key)
 
@@ -105,7 +108,18 @@ def cpu_baseline(w, x, heads=3):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"{heads} query heads (b=0, h=0..{heads - 1}) of the workload at full N={w.N}: "
                       f"fp64 forward + backward, {dt:.1f} s wall; metric FLOPs of those heads",
-            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
+            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -163,6 +177,22 @@ def main():
     bwd = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     cvt = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
 
+    # Cold caches: before each of these steps a 512 MiB fill (twice the
+    # 256 MB Infinity Cache, far above the L2s) evicts the inputs; only the
+    # step itself is timed, with events.
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 27, device=dev, dtype=torch.float32)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.cold_steps)]
+        for i in range(args.cold_steps):
+            flush.fill_(float(i))
+            step(cev[i])
+        torch.cuda.synchronize()
+        cms = sorted(e[0].elapsed_time(e[3]) for e in cev)[args.cold_steps // 2]
+        cold = {"ms_per_step": round(cms, 4), "tflops": round(w.flops() / (cms * 1e-3) / 1e12, 2),
+                "steps": args.cold_steps, "statistic": "median of event-timed steps, each after a 512 MiB fill"}
+        del flush
+
     # The forward (attn_fwd_stats) is a support step outside the timed
     # backward step; timed here on its own for reference.
     fe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -181,7 +211,7 @@ def main():
     esz = 2 if w.dtype == "bf16" else 4
     pre_bytes = 2 * B * H * N * d * esz + B * H * N * 4           # read O, dO; write D
     cvt_bytes = B * H * N * d * 4 + B * H * N * d * esz           # read dQaccum; write dQ
-    traffic = measured_traffic()
+    traffic = measured_traffic(w.name)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -210,6 +240,7 @@ def main():
         "stream_kernels_GBs": {"bwd_preprocess": round(pre_bytes / (pre * 1e-3) / 1e9, 1),
                                "bwd_dq_convert": round(cvt_bytes / (cvt * 1e-3) / 1e9, 1),
                                "peak": PEAK_HBM_GBS},
+        "cold_cache": cold,
         "forward": {"kernel": "attn_fwd_stats (not part of the timed step)", "ms": round(fwd_ms, 4),
                     "tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 1), "flops": "4/10 of the backward metric FLOPs"},
     }

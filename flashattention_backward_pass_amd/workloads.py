@@ -92,6 +92,9 @@ WORKLOADS = {
         # offset fixed.
         _wl("bf16_dropout0.1_causal_b1h8_n16384_d128", 1, 8, 8, 16384, 128, "bf16", True, 0.0, 1.0, 1006,
             dropout=(0.1, 0x5EED0000_00001006, 0)),
+        # One GPU's share of the long workload sharded by heads over 8 GPUs:
+        # a single head at its full length.
+        _wl("bf16_causal_b1h1_n16384_d128", 1, 1, 1, 16384, 128, "bf16", True, 0.0, 1.0, 1007),
     ]
 }
 WORKLOAD_ORDER = list(WORKLOADS)
