@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 DEFAULT_WORKLOAD = "bf16_causal_b1h8_n16384_d128"
 BWD_SOURCES = [os.path.join(ROOT, "flashattention_backward_pass_amd", "csrc", f)
-               for f in ("bwd_dkdv.hip", "bwd_dq.hip", "mfma_common.h", "philox.h")]
+               for f in ("bwd_dkdv.hip", "bwd_dkdv_block.h", "bwd_dq.hip", "bwd_dq_block.h", "mfma_common.h", "philox.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_traffic.json")
 
 

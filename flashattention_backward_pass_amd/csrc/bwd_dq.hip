@@ -1,282 +1,20 @@
-// bf16 dQ kernel on gfx950 matrix cores: query blocks outer, key blocks inner.
-//
-// dQ_i = sum_j dS_ij K_j ("解析 FlashAttention（3）：FlashAttention-v1 反向传播",
-// eq (15), without the scale tau, which the convert kernel applies).  The
-// pages accumulate dQ across key blocks with fp32 atomics into a global
-// buffer (Inference Cookbook "反向传播算法详解", section 6.2).  On MI355X every
-// global float atomic is executed at the memory side rather than in L2, which
-// caps that path near 1.3 TB/s of update traffic; this kernel instead gives
-// each workgroup a whole block of query rows, recomputes S and dP for them
-// (P from the saved LSE, section 1.2 of the Cookbook page), and keeps dQ in
-// registers over all key blocks, so dQaccum is written once with plain
-// stores and the result does not depend on any summation order across
-// workgroups.
-//
-// Per workgroup: 128 query rows of one query head (wave w owns rows
-// 32w..32w+31), key blocks of 64 streamed through double-buffered LDS tiles.
-// Per key block and 32-key half:
-//   S^T  = K Q^T      (keys x queries; Q rows of this wave in registers)
-//   dP^T = V dO^T
-//   P = exp2(S' tau log2e - LSE log2e), dS = P o (dP - D) [o (1 - tanh^2)]
-//   dQ  += dS K       (dS^T accumulator layout = A operand with queries on
-//                      lanes; K^T read transposed from the row-major K tile)
-// Computing S^T rather than S puts one query per lane, so LSE and D are one
-// register each.  Wave priorities: S/dP chain 0, softmax 2, dQ chain 1.
-// Dropout (FlashAttention-v1 page, eq (12)): dP^T is multiplied by the
-// replayed mask Z before dS; the quad of lanes holding 4 consecutive queries
-// evaluates the 8 generator calls of a 32-key half together (philox.h).
-#include <type_traits>
-
-#include "fabwd_launch.h"
-#include "mfma_common.h"
+// bf16 dQ kernel: one workgroup per work unit of dq_block (bwd_dq_block.h).
+#include "bwd_dq_block.h"
 
 namespace fabwd {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kPF = 2;   // S/dP steps whose operand reads run ahead of their use
-constexpr int BQ = 128;  // query rows per workgroup
-constexpr int BK = 64;   // keys per inner step
+using dq::BQ;
+using dq::kThreads;
 
-// Key k is visible to query q iff q - wl <= k <= q + wr and k < N (causal:
-// wr = 0; an unbounded side is N).
 template <int D, bool SOFTCAP, bool DROPOUT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     float* __restrict__ dQacc, int H, int H_kv, int N, int BHq, float scale, float softcap, int wl, int wr,
     Dropout drop) {
-  constexpr int KC = D / 16;
-  constexpr int NT = D / 32;
-  // Double buffers as separate variables: the compiler gives each LDS
-  // variable its own alias scope, so reads of one buffer do not wait for the
-  // asynchronous copies still landing in the other.
-  // K and V of one buffer share a variable (copied and read together): a V
-  // address is then the K address plus an immediate offset.
-  __shared__ __attribute__((aligned(1024))) uint16_t sKV0[2 * BK * D], sKV1[2 * BK * D];
-  uint16_t* const sK0 = sKV0;
-  uint16_t* const sK1 = sKV1;
-  uint16_t* const sV0 = sKV0 + BK * D;
-  uint16_t* const sV1 = sKV1 + BK * D;
-  auto bufsel = [](auto bufc, auto* a0, auto* a1) {
-    if constexpr (decltype(bufc)::value == 0) return a0;
-    else return a1;
-  };
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, g = lane >> 5;
-  const int j16 = lane & 15, h16 = (lane >> 4) & 1;
-
-  // Work unit: the key/value head varies fastest, so that with the
-  // round-robin placement of workgroups on the 8 XCDs the query heads of one
-  // group share an XCD (and its L2 holds their K, V); then the query head in
-  // the group; query blocks vary slowest, last (heaviest under a causal
-  // mask) first.
-  const int n_qblk = (N + BQ - 1) / BQ;
-  const int G = H / H_kv;
-  const int BHkv = BHq / G;
-  const int kvu = int(blockIdx.x % unsigned(BHkv));
-  const int rest = int(blockIdx.x / unsigned(BHkv));
-  const int b = kvu / H_kv, hk = kvu % H_kv;
-  const int h = hk * G + rest % G;
-  const int bhq = b * H + h;
-  const int iblk = n_qblk - 1 - rest / G;
-  const int q0 = iblk * BQ;
-  const int64_t q_off = (int64_t(b) * H + h) * N;
-  const int64_t kv_off = (int64_t(b) * H_kv + hk) * N;
-  const int my_q = q0 + 32 * w + l32;  // query row owned by this lane
-  const int my_qc = min(my_q, N - 1);
-
-  // Q and dO rows of this lane (B operands of S^T and dP^T), LSE and D.
-  bf16x8_t qreg[KC], doreg[KC];
-#pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    qreg[c] = load_bf16x8(Q + (q_off + my_qc) * D + 16 * c + 8 * g);
-    doreg[c] = load_bf16x8(dO + (q_off + my_qc) * D + 16 * c + 8 * g);
-  }
-  const float nl2 = -LSE[q_off + my_qc] * kLog2e;
-  const float dval = Dv[q_off + my_qc];
-  const float zs = scale * kLog2e;
-  const float cap_k = SOFTCAP ? 2.f * kLog2e / softcap : 0.f;  // tanh(x / c) = tanh_scaled(x, cap_k)
-  const float cap_zs = softcap * zs;
-
-  f32x16_t dq_acc[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) dq_acc[n] = f32x16_t{};
-
-  // LDS element offsets of this lane's operand reads within a K or V block.
-  // The swizzle depends on the row mod 16 only, so rows 32 s + l32 (row
-  // reads) and 32 s + 16 u + 4 g + j16/4 (+ 8) (transposed reads) are these
-  // offsets plus a multiple of 16 D.  The empty asm hides their bits from the
-  // compiler: otherwise it forms the V and second-buffer addresses with a
-  // bitwise or, which an LDS instruction cannot take as its immediate offset,
-  // and keeps a register for every (buffer, tensor, half) variant.
-  int roff[KC], toff[NT][2];
-#pragma unroll
-  for (int c = 0; c < KC; ++c) {
-    roff[c] = swz_off<D>(l32, 2 * c + g, 0);
-    asm volatile("" : "+v"(roff[c]));
-  }
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int ch = 4 * n + 2 * h16 + ((j16 & 3) >> 1);
-    const int sub = 4 * (j16 & 1);
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      toff[n][v] = swz_off<D>(4 * g + (j16 >> 2) + 8 * v, ch, sub);
-      asm volatile("" : "+v"(toff[n][v]));
-    }
-  }
-
-  // Key blocks [s_lo, s_hi) hold every key that some row of this block sees.
-  const int q_hi = min(q0 + BQ, N) - 1;  // last valid row
-  const int s_lo = max(0, q0 - wl) / BK;
-  const int s_hi = (min(N, q_hi + wr + 1) + BK - 1) / BK;
-
-  // Per-lane byte offsets of the K/V block copies: slab I = s*4 + w covers
-  // rows I*RPS ..; lane L fills physical chunk L % (D/8) of row I*RPS + L/(D/8),
-  // i.e. logical chunk (L % (D/8)) ^ swz(row).
-  constexpr int RPS = 1024 / (2 * D);
-  constexpr int NSLAB = BK / RPS / 4;
-  int dma_voff[NSLAB];
-#pragma unroll
-  for (int s = 0; s < NSLAB; ++s) {
-    const int row = (s * 4 + w) * RPS + lane / (D / 8);
-    dma_voff[s] = (row * D + 8 * ((lane % (D / 8)) ^ swz<D>(row))) * 2;
-  }
-  // Copy key/value block `step` into LDS buffer step%2 with buffer loads that
-  // write LDS directly (scalar base per block; a ragged block clamps its rows
-  // to the last valid key).
-  auto issue = [&](auto bufc, int step) {
-    const int kb = step * BK;
-    const int rows = min(BK, N - kb);
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(K + (kv_off + kb) * D), 0, rows * D * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(V + (kv_off + kb) * D), 0, rows * D * 2, 0x00020000);
-#pragma unroll
-    for (int s = 0; s < NSLAB; ++s) {
-      int voff = dma_voff[s];
-      if (rows < BK) {
-        const int row = min((s * 4 + w) * RPS + lane / (D / 8), rows - 1);
-        voff = (row * D + 8 * ((lane % (D / 8)) ^ swz<D>((s * 4 + w) * RPS + lane / (D / 8)))) * 2;
-      }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)&bufsel(bufc, sK0, sK1)[(s * 4 + w) * 512], 16, voff,
-                                               0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)&bufsel(bufc, sV0, sV1)[(s * 4 + w) * 512], 16, voff,
-                                               0, 0, 0);
-    }
-  };
-
-  // One key block in buffer BUF (the loop below alternates the buffers with
-  // compile-time selection, so every LDS access names one variable).
-  auto body = [&](auto bufc, int step) __attribute__((always_inline)) {
-    using NB = std::integral_constant<int, 1 - decltype(bufc)::value>;
-    const uint16_t* sk = bufsel(bufc, sK0, sK1);
-    const uint16_t* sv = bufsel(bufc, sV0, sV1);
-    const int kb = step * BK;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // block `step` in this buffer; the other buffer no longer read
-    if (step + 1 < s_hi) issue(NB{}, step + 1);
-    // Unmasked: every key of the block is visible to every row of this block.
-    const bool masked = kb + BK > N || kb < q_hi - wl || kb + BK - 1 > q0 + wr;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      // S^T, dP^T for keys kb + 32 s .. + 31 (rows) x this wave's 32 queries (columns).
-      f32x16_t st = {}, dpt = {};
-      __builtin_amdgcn_s_setprio(0);
-      // The reads of step c + kPF are issued before the matrix instructions of
-      // step c (the fences keep the scheduler from sinking them to their use).
-      bf16x8_t kop[KC], vop[KC];
-      auto read_ops = [&](int c) {
-        kop[c] = *reinterpret_cast<const bf16x8_t*>(&sk[roff[c] + 32 * s * D]);
-        vop[c] = *reinterpret_cast<const bf16x8_t*>(&sv[roff[c] + 32 * s * D]);
-      };
-#pragma unroll
-      for (int c = 0; c < kPF; ++c) read_ops(c);
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        if (c + kPF < KC) read_ops(c + kPF);
-        __builtin_amdgcn_sched_barrier(0);
-        st = mfma32(kop[c], qreg[c], st);
-        dpt = mfma32(vop[c], doreg[c], dpt);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // The two waves of a SIMD overlap one's softmax with the other's matrix
-      // instructions; the softmax phase (mask generator included) issues at
-      // the higher priority so it finishes while the matrix core is busy.
-      __builtin_amdgcn_s_setprio(2);
-      DropBits keep;
-      if (DROPOUT) {
-        DropQueryLane gen;
-        gen.init(drop, uint32_t(bhq), kb + 32 * s, my_q, lane);
-        gen.rounds(0, 10);
-        keep = gen.finish(lane);
-      }
-      // Register r: key kb + 32 s + 8(r/4) + 4g + r%4, query my_q.  dS is
-      // computed for every key, then masked keys are set to 0 in one pass
-      // under a single uniform branch (a test inside this loop becomes a
-      // branch per element).  The select discards whatever a masked key
-      // produced, inf or NaN included.
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float dt = 1.f;
-        float p;
-        if (SOFTCAP) {
-          const float th = tanh_scaled(st[r], cap_k);
-          dt = fmaf(-th, th, 1.f);
-          p = fast_exp2(fmaf(th, cap_zs, nl2));
-        } else {
-          p = fast_exp2(fmaf(st[r], zs, nl2));
-        }
-        float dp = dpt[r];
-        if (DROPOUT) dp = keep.keep(r, drop.keep_t) ? dp * drop.scale : 0.f;
-        float ds = p * (dp - dval);
-        if (SOFTCAP) ds *= dt;
-        st[r] = ds;
-      }
-      if (masked) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb + 32 * s + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= N || key > my_q + wr || key < my_q - wl) st[r] = 0.f;
-        }
-      }
-      bf16x8_t dsf[2];
-      dsf[0] = pack_bf16x8(st, 0);
-      dsf[1] = pack_bf16x8(st, 8);
-      __builtin_amdgcn_s_setprio(1);
-      // dQ += dS K over these 32 keys: K operand rows 32 s + 16u + 4g + (0..3) and +8.
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int rb = (32 * s + 16 * u) * D;
-          const bf16x8_t kop = cat8(lds_read_tr(&sk[toff[n][0] + rb]), lds_read_tr(&sk[toff[n][1] + rb]));
-          dq_acc[n] = mfma32(dsf[u], kop, dq_acc[n]);
-        }
-      }
-    }
-  };
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  if (s_lo < s_hi) issue(B0{}, s_lo);
-  for (int step = s_lo; step < s_hi; step += 2) {
-    body(B0{}, step);
-    if (step + 1 < s_hi) body(B1{}, step + 1);
-  }
-
-  // dQaccum rows of this wave (unscaled).  Register r: row 32w + 8(r/4) + 4g + r%4.
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int q = q0 + 32 * w + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (q < N) dQacc[(q_off + q) * D + 32 * n + l32] = dq_acc[n][r];
-    }
-  }
+  dq::dq_block<D, SOFTCAP, DROPOUT>(Q, K, V, dO, LSE, Dv, dQacc, H, H_kv, N, BHq, scale, softcap, wl, wr, drop, blockIdx.x);
 }
 
 template <int D, bool SOFTCAP, bool DROPOUT>
