@@ -42,11 +42,12 @@ COMMON_FLAGS = [
 ]
 
 
-# Per-file flags.  bwd_dkdv.hip keeps every matrix accumulator in VGPRs
+# Per-file flags.  The dK/dV kernel keeps every matrix accumulator in VGPRs
 # (the softmax-gradient VALU work reads S and dP straight from them; the
 # K/V operand slices are pinned to AGPRs in the source).
 FILE_FLAGS = {
     "bwd_dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "bwd_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],  # runs the dK/dV work units too
 }
 
 

@@ -52,6 +52,15 @@ __global__ __launch_bounds__(256) void dkdv_split_sum_kernel(const float* __rest
   *reinterpret_cast<u32x4_t*>(dV + i) = vo;
 }
 
+}  // namespace
+
+int dkdv_split_count(const Problem& p, bool have_scratch) {
+  const int64_t units = int64_t(p.B) * p.H_kv * ((p.N + BC - 1) / BC);
+  return (have_scratch && p.H / p.H_kv >= 4 && units < 1024) ? 2 : 1;
+}
+
+namespace {
+
 template <int D, bool SOFTCAP, bool DROPOUT>
 hipError_t dkdv_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                   const float* Dv, void* dK, void* dV, float* scratch, hipStream_t s) {
@@ -62,8 +71,7 @@ hipError_t dkdv_t(const Problem& p, const void* Q, const void* K, const void* V,
   // the heads out over two workgroups; their fp32 partials fit in `scratch`
   // (B*H*N*d floats) because 2 splits x (dK, dV) x B*H_kv*N*d <= B*H*N*d
   // when G >= 4.
-  const int G = p.H / p.H_kv;
-  const int n_split = (scratch != nullptr && G >= 4 && int64_t(BH) * n_kblk < 1024) ? 2 : 1;
+  const int n_split = dkdv_split_count(p, scratch != nullptr);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, SOFTCAP, DROPOUT>), dim3(unsigned(BH) * unsigned(n_kblk) * unsigned(n_split)),
                      dim3(kThreads), 0, s, static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K),
                      static_cast<const bf16_t*>(V), static_cast<const bf16_t*>(dO), LSE, Dv,

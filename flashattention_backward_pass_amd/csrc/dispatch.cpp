@@ -16,6 +16,8 @@ hipError_t launch_bwd(const Problem& p, const void* Q, const void* K, const void
   (void)hipGetLastError();
   // bf16: matrix-core kernels; fp32: vector-ALU kernel (same fp32 peak on MI355X).
   if (p.dtype == 1) {
+    // Few work units: both kinds in one launch, so that they share the chip.
+    if (bwd_fused_fits(p)) return launch_bwd_fused_mfma(p, Q, K, V, dO, LSE, D, dK, dV, dQacc, s);
     // dQaccum is overwritten by the dQ kernel afterwards: until then the
     // dK/dV kernel may keep partial sums in it.
     hipError_t e = launch_bwd_dkdv_mfma(p, Q, K, V, dO, LSE, D, dK, dV, dQacc, s);

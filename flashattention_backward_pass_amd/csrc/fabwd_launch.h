@@ -61,5 +61,15 @@ hipError_t launch_bwd_dkdv_mfma(const Problem& p, const void* Q, const void* K, 
                                 hipStream_t s);
 hipError_t launch_bwd_dq_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                               const float* LSE, const float* D, float* dQacc, hipStream_t s);
+// Workgroups sharing each (b, kv head, key block) unit of the dK/dV kernel:
+// 2 for grouped heads (G >= 4) with few units, whose fp32 partials then use
+// the scratch space (dQaccum) before the dQ kernel overwrites it; else 1.
+int dkdv_split_count(const Problem& p, bool have_scratch);
+// Both kernels' work units in one launch, for problems too small to fill
+// the chip with either kernel alone (bwd_fused_fits).  Requires
+// dkdv_split_count(p, true) == 1.
+bool bwd_fused_fits(const Problem& p);
+hipError_t launch_bwd_fused_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
+                                 const float* LSE, const float* D, void* dK, void* dV, float* dQacc, hipStream_t s);
 
 }  // namespace fabwd
