@@ -76,6 +76,27 @@ def test_long_sequence_sampled_heads():
             assert e <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("cap,drop", [(0.0, None), (10.0, (0.1, 77, 2))], ids=["plain", "softcap_dropout"])
+def test_standalone_kernels_d64(cap, drop):
+    """B=4 H=8 N=2048 d=64 causal: 512 dK/dV and 512 dQ work units, more than
+    the combined launch takes, so the two kernels run one after the other.
+    Full oracle on the first and last heads."""
+    w = workloads.custom(4, 8, 8, 2048, 64, "bf16", True, cap, seed=64, name="standalone_d64", dropout=drop)
+    x = workloads.make_inputs(w)
+    got = run_gpu(w, x)
+    for b, g in ((0, 0), (w.B - 1, w.H_kv - 1)):
+        ref = oracle_kv_heads(w, x, b, [g])
+        for n in ("O", "LSE", "dQ"):
+            for h, r in ref[n].items():
+                e = rel_err(to_np(got[n][b, h]), r)
+                print(f"[{w.name}] b{b} head {h} {n}={e:.2e}", flush=True)
+                assert e <= TOL[w.dtype], n
+        for n in ("dK", "dV"):
+            e = rel_err(to_np(got[n][b, g]), ref[n][g])
+            print(f"[{w.name}] b{b} kv head {g} {n}={e:.2e}", flush=True)
+            assert e <= TOL[w.dtype], n
+
+
 def test_preprocess_matches_rowsum_of_same_inputs():
     """D from the GPU equals the fp64 row dot product of the very same O and dO."""
     w = workloads.WORKLOADS[workloads.WORKLOAD_ORDER[2]]
