@@ -251,15 +251,21 @@ __device__ __forceinline__ void dq_block(
       dsf[0] = pack_bf16x8(st, 0);
       dsf[1] = pack_bf16x8(st, 8);
       __builtin_amdgcn_s_setprio(1);
-      // dQ += dS K over these 32 keys: K operand rows 32 s + 16u + 4g + (0..3) and +8.
+      // dQ += dS K over these 32 keys: K operand rows 32 s + 16u + 4g + (0..3)
+      // and +8; step i = 2n + u, its operand read kPF steps ahead.
+      bf16x8_t kt[2 * NT];
+      auto read_kt = [&](int i) {
+        const int rb = (32 * s + 16 * (i & 1)) * D;
+        kt[i] = cat8(lds_read_tr(&sk[toff[i >> 1][0] + rb]), lds_read_tr(&sk[toff[i >> 1][1] + rb]));
+      };
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
+      for (int i = 0; i < kPF; ++i) read_kt(i);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int rb = (32 * s + 16 * u) * D;
-          const bf16x8_t kop = cat8(lds_read_tr(&sk[toff[n][0] + rb]), lds_read_tr(&sk[toff[n][1] + rb]));
-          dq_acc[n] = mfma32(dsf[u], kop, dq_acc[n]);
-        }
+      for (int i = 0; i < 2 * NT; ++i) {
+        if (i + kPF < 2 * NT) read_kt(i + kPF);
+        __builtin_amdgcn_sched_barrier(0);
+        dq_acc[i >> 1] = mfma32(dsf[i & 1], kt[i], dq_acc[i >> 1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
