@@ -38,7 +38,7 @@ namespace fabwd {
 namespace dq {
 
 constexpr int kThreads = 256;
-constexpr int kPF = 2;   // S/dP steps whose operand reads run ahead of their use
+constexpr int kPF = 2;   // matrix steps (S/dP and dQ chains) whose operand reads run ahead
 constexpr int BQ = 128;  // query rows per workgroup
 constexpr int BK = 64;   // keys per inner step
 
