@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       mx = fmaxf(mx, st[r]);
     }
     if (!SOFTCAP) mx *= zs;  // -inf stays -inf
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_lane_pair32(mx);
     // Lazy rescale: raise m only when a score exceeds it by more than kLazy.
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
       const float m_new = mx > m + kLazy ? mx : m;
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // Epilogue: l over both key groups; O = O^T / l (4 consecutive d per
   // register group), LSE = (m + log2 l) ln 2.
-  l += __shfl_xor(l, 32);
+  l = sum_lane_pair32(l);
   if (my_q < N) {
     const float inv = (DROPOUT ? drop.scale : 1.f) / l;
 #pragma unroll

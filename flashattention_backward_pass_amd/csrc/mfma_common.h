@@ -26,6 +26,31 @@ __device__ __forceinline__ bf16x4_t lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
 }
 
+// Lanes l and l ^ 32 hold the two halves of one accumulator column: combine
+// their values with one gfx950 v_permlane32_swap (no LDS round trip).  The
+// instruction exchanges lanes 32-63 of its first operand with lanes 0-31 of
+// its second; with v in both, lane l < 32 receives (v[l], v[l + 32]) and
+// lane l >= 32 receives (v[l - 32], v[l]).  (The two results are copied to
+// scalars before the bit cast: a bit cast of a vector element reads the
+// vector's first element.)
+__device__ __forceinline__ void lane_pair32(float v, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float max_lane_pair32(float v) {
+  float a, b;
+  lane_pair32(v, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_lane_pair32(float v) {
+  float a, b;
+  lane_pair32(v, a, b);
+  return a + b;
+}
+
 __device__ __forceinline__ bf16x8_t cat8(bf16x4_t a, bf16x4_t b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
