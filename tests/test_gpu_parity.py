@@ -78,10 +78,10 @@ def test_long_sequence_sampled_heads():
 
 @pytest.mark.parametrize("cap,drop", [(0.0, None), (10.0, (0.1, 77, 2))], ids=["plain", "softcap_dropout"])
 def test_standalone_kernels_d64(cap, drop):
-    """B=4 H=8 N=2048 d=64 causal: 512 dK/dV and 512 dQ work units, more than
+    """B=8 H=8 N=2048 d=64 causal: 1024 dK/dV and 1024 dQ work units, more than
     the combined launch takes, so the two kernels run one after the other.
     Full oracle on the first and last heads."""
-    w = workloads.custom(4, 8, 8, 2048, 64, "bf16", True, cap, seed=64, name="standalone_d64", dropout=drop)
+    w = workloads.custom(8, 8, 8, 2048, 64, "bf16", True, cap, seed=64, name="standalone_d64", dropout=drop)
     x = workloads.make_inputs(w)
     got = run_gpu(w, x)
     for b, g in ((0, 0), (w.B - 1, w.H_kv - 1)):
