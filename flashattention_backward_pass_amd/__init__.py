@@ -147,6 +147,15 @@ def _params_from(q, k, causal, scale, softcap, deterministic=False, window=None,
                        window, dropout)
 
 
+def _expect(t, shape, dtype, name):
+    """Shape and dtype of a buffer the kernels read or write: the C interface
+    receives bare pointers, so a wrong size must be caught here."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
 def _check(status: int, where: str):
     if status != ATTN_OK:
         raise AttnError(status, where)
@@ -155,6 +164,10 @@ def _check(status: int, where: str):
 def attn_fwd_stats(q, k, v, o, lse, *, causal=False, scale=None, softcap=0.0, stream=None, window=None,
                    dropout=None):
     p = _params_from(q, k, causal, scale, softcap, window=window, dropout=dropout)
+    f32 = _torch().float32
+    _expect(v, k.shape, q.dtype, "V")
+    _expect(o, q.shape, q.dtype, "O")
+    _expect(lse, q.shape[:3], f32, "LSE")
     lib = load_library()
     _check(lib.attn_fwd_stats(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(stream)),
            "attn_fwd_stats")
@@ -164,6 +177,10 @@ def attn_bwd_preprocess(o, do, D, dq_accum, *, H_kv=None, causal=False, scale=No
                         window=None):
     B, H, N, d = o.shape
     p = make_params(B, H, H_kv or H, N, d, _dtype_code(o), causal, scale, softcap, window=window)
+    f32 = _torch().float32
+    _expect(do, o.shape, o.dtype, "dO")
+    _expect(D, (B, H, N), f32, "D")
+    _expect(dq_accum, o.shape, f32, "dQaccum")
     lib = load_library()
     _check(lib.attn_bwd_preprocess(ctypes.byref(p), _ptr(o), _ptr(do), _ptr(D), _ptr(dq_accum), _stream(stream)),
            "attn_bwd_preprocess")
@@ -172,6 +189,14 @@ def attn_bwd_preprocess(o, do, D, dq_accum, *, H_kv=None, causal=False, scale=No
 def attn_bwd(q, k, v, do, lse, D, dq_accum, dk, dv, *, causal=False, scale=None, softcap=0.0, stream=None,
              deterministic=False, window=None, dropout=None):
     p = _params_from(q, k, causal, scale, softcap, deterministic, window, dropout)
+    f32 = _torch().float32
+    _expect(v, k.shape, q.dtype, "V")
+    _expect(do, q.shape, q.dtype, "dO")
+    _expect(lse, q.shape[:3], f32, "LSE")
+    _expect(D, q.shape[:3], f32, "D")
+    _expect(dq_accum, q.shape, f32, "dQaccum")
+    _expect(dk, k.shape, q.dtype, "dK")
+    _expect(dv, k.shape, q.dtype, "dV")
     lib = load_library()
     _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D),
                         _ptr(dq_accum), _ptr(dk), _ptr(dv), _stream(stream)), "attn_bwd")
@@ -180,6 +205,7 @@ def attn_bwd(q, k, v, do, lse, D, dq_accum, dk, dv, *, causal=False, scale=None,
 def attn_bwd_dq_convert(dq_accum, dq, *, scale=None, stream=None):
     B, H, N, d = dq.shape
     p = make_params(B, H, H, N, d, _dtype_code(dq), False, scale, 0.0)
+    _expect(dq_accum, dq.shape, _torch().float32, "dQaccum")
     lib = load_library()
     _check(lib.attn_bwd_dq_convert(ctypes.byref(p), _ptr(dq_accum), _ptr(dq), _stream(stream)),
            "attn_bwd_dq_convert")

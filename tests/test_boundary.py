@@ -171,6 +171,46 @@ def test_binding_fails_loudly_without_library(tmp_path):
         fab._lib = saved
 
 
+def _bufs(B=1, H=4, Hkv=2, N=8, d=64):
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    q = torch.zeros(B, H, N, d, dtype=bf)
+    k = torch.zeros(B, Hkv, N, d, dtype=bf)
+    return dict(q=q, k=k, v=k.clone(), o=q.clone(), do=q.clone(), lse=torch.zeros(B, H, N, dtype=f32),
+                D=torch.zeros(B, H, N, dtype=f32), acc=torch.zeros(B, H, N, d, dtype=f32), dk=k.clone(),
+                dv=k.clone(), dq=q.clone())
+
+
+@pytest.mark.parametrize("bad", ["v", "do", "lse", "D", "acc", "dk", "dv"])
+def test_binding_checks_every_buffer_of_attn_bwd(bad):
+    """The C interface gets bare pointers: the binding rejects any buffer whose
+    shape or dtype does not match the problem before the library is called."""
+    import torch
+    t = _bufs()
+    wrong = dict(t)
+    x = t[bad]
+    wrong[bad] = torch.zeros(*x.shape[:-1], x.shape[-1] + 1, dtype=x.dtype)  # one element too many per row
+    with pytest.raises(ValueError, match="shape"):
+        fab.attn_bwd(wrong["q"], wrong["k"], wrong["v"], wrong["do"], wrong["lse"], wrong["D"], wrong["acc"],
+                     wrong["dk"], wrong["dv"])
+    wrong[bad] = x.to(torch.float16)
+    with pytest.raises(TypeError, match="dtype"):
+        fab.attn_bwd(wrong["q"], wrong["k"], wrong["v"], wrong["do"], wrong["lse"], wrong["D"], wrong["acc"],
+                     wrong["dk"], wrong["dv"])
+
+
+def test_binding_checks_buffers_of_the_other_entry_points():
+    import torch
+    t = _bufs()
+    short = torch.zeros(1, 4, 7, dtype=torch.float32)
+    with pytest.raises(ValueError, match="LSE"):
+        fab.attn_fwd_stats(t["q"], t["k"], t["v"], t["o"], short)
+    with pytest.raises(ValueError, match="D"):
+        fab.attn_bwd_preprocess(t["o"], t["do"], short, t["acc"], H_kv=2)
+    with pytest.raises(ValueError, match="dQaccum"):
+        fab.attn_bwd_dq_convert(t["acc"][:, :, :7], t["dq"])
+
+
 @pytest.mark.parametrize("window", [(0, 0), (5, -1), (-1, 3), (1 << 24, 7)])
 def test_windows_accepted(lib, window):
     # Valid windows on an empty problem: every argument is checked, nothing runs.
