@@ -126,7 +126,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the backward library is a "
-              "single-GPU path; see DESIGN.md for how it would shard.", file=sys.stderr)
+              "single-GPU path (it would shard by whole key/value heads, one share per GPU, with no "
+              "communication).", file=sys.stderr)
         sys.exit(2)
     import torch
 
