@@ -41,7 +41,7 @@ Readings taken where the pages are silent or ambiguous:
     O = (P o Z) V, and give dV = (P o Z)^T dO (eq (10)) and dP = (dO V^T) o Z
     (eq (12)); D = rowsum(dO o O) and dZ = P o (dP - D) are unchanged
     (eqs (13), (14)).  The pages fix no generator: oracle/philox.py states the
-    Philox4x32-10 stream this build uses.  LSE stays that of the undropped P.
+    Philox4x32-10 stream that is replayed.  LSE stays that of the undropped P.
 
 Parity pins: tests/test_oracle_*.py (N=2, d=2 hand expansions of [FA1]
 section 2, central finite differences of <dO, O>, invariants, closed forms,

@@ -19,9 +19,9 @@ the round key, and permutes the words; the key advances by the Weyl constants
 (W0, W1) between rounds.  W = 32 is the instance used; W = 64 is kept so the
 round structure can be checked against numpy's independent Philox4x64-10.
 
-Element -> random bits (this build's own choice, shared with the kernels by
-specification only).  For query head bh = b * H + h, query row q and key k,
-one Philox4x32-10 call with
+Element -> random bits (a choice the pages leave open; the kernels follow the
+same statement, with code of their own).  For query head bh = b * H + h,
+query row q and key k, one Philox4x32-10 call with
     counter = (k >> 1, q >> 2, bh, offset),  key = (seed mod 2^32, seed >> 32)
 returns words x0..x3; the element's 16-bit value is u = half (k & 1) of word
 (q & 3) (half 0 = low 16 bits).  One call covers a block of 4 query rows by 2
