@@ -117,6 +117,9 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
   const int64_t kv_off = (int64_t(b) * H_kv + hk) * N;  // row offset of this kv head
   const int kw = w * 32;                                 // this wave's first key in the block
   const int my_key = k0 + kw + l32;                      // key owned by this lane in GEMM 1/2
+  // Queries q that see my_key: q - wl <= my_key <= q + wr, q < N, my_key < N.
+  const int vq_lo = max(0, my_key - wr);
+  const int vq_len = my_key < N ? max(0, min(N - 1, my_key + wl) - vq_lo + 1) : 0;
 
   // K_j and -V_j slices: B operands of GEMM 1/2, resident for the whole loop.
   // Keys past N read row N-1: their P is masked to 0, so they contribute nothing.
@@ -269,13 +272,15 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
     // Masked tiles: positions outside the causal triangle or past N start S
     // at -inf (so P = exp2(-inf) = 0 and dS = 0); with a soft cap the
     // subtracted LSE becomes +inf instead.  Applied to the initial values only.
+    // The queries that see this lane's key form one range [vq_lo, vq_lo +
+    // vq_len) (empty past N), so the test is one unsigned compare per element
+    // (a chain of compares was compiled into a branch per element).
     auto mask_init = [&](f32x16_t& a, int h) {
       const float fill = SOFTCAP ? __builtin_inff() : -__builtin_inff();
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qg = q0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool ok = qg < N && my_key < N && my_key <= qg + wr && my_key >= qg - wl;
-        a[r] = ok ? a[r] : fill;
+        a[r] = unsigned(qg - vq_lo) < unsigned(vq_len) ? a[r] : fill;
       }
     };
     // The softmax gradient of one element in three steps, software-pipelined
