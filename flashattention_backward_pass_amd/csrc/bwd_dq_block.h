@@ -91,6 +91,10 @@ __device__ __forceinline__ void dq_block(
   const int64_t kv_off = (int64_t(b) * H_kv + hk) * N;
   const int my_q = q0 + 32 * w + l32;  // query row owned by this lane
   const int my_qc = min(my_q, N - 1);
+  // Keys k that my_q sees form one range: my_q - wl <= k <= my_q + wr, k < N
+  // (one unsigned compare per element in the mask pass).
+  const int vk_lo = max(0, my_q - wl);
+  const int vk_len = max(0, min(N - 1, my_q + wr) - vk_lo + 1);
 
   // Q and dO rows of this lane (B operands of S^T and dP^T), LSE and D.
   bf16x8_t qreg[KC], doreg[KC];
@@ -244,7 +248,7 @@ __device__ __forceinline__ void dq_block(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb + 32 * s + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= N || key > my_q + wr || key < my_q - wl) st[r] = 0.f;
+          st[r] = unsigned(key - vk_lo) < unsigned(vk_len) ? st[r] : 0.f;
         }
       }
       bf16x8_t dsf[2];
