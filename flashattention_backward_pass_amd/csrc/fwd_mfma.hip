@@ -79,6 +79,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int64_t kv_off = (int64_t(b) * H_kv + hk) * N;
   const int my_q = q0 + 32 * w + l32;  // query of this lane
   const int qc = min(my_q, N - 1);
+  // Keys k that my_q sees form one range (my_q - wl <= k <= my_q + wr, k < N):
+  // one unsigned compare per element on masked blocks.
+  const int vk_lo = max(0, my_q - wl);
+  const int vk_len = max(0, min(N - 1, my_q + wr) - vk_lo + 1);
 
   // Q row of this lane: B operand of S^T = K Q^T (k = d).
   bf16x8_t qreg[KC];
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kb + 32 * s + 8 * (r >> 2) + 4 * g + (r & 3);
-        st[r] = (key < N && key <= my_q + wr && key >= my_q - wl) ? 0.f : -__builtin_inff();
+        st[r] = unsigned(key - vk_lo) < unsigned(vk_len) ? 0.f : -__builtin_inff();
       }
     }
     __builtin_amdgcn_s_setprio(0);
