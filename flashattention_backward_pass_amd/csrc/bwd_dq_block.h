@@ -109,6 +109,14 @@ __device__ __forceinline__ void dq_block(
   const float cap_k = SOFTCAP ? 2.f * kLog2e / softcap : 0.f;  // tanh(x / c) = tanh_scaled(x, cap_k)
   const float cap_zs = softcap * zs;
 
+  // -D_q in every register: without dropout the first dP^T instruction of a
+  // key block takes it as the accumulator input, so the chain ends with
+  // dP - D (this lane's query, and so D, is the same for every key) and the
+  // softmax step saves a subtraction per element.
+  f32x16_t neg_d;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) neg_d[r] = -dval;
+
   f32x16_t dq_acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) dq_acc[n] = f32x16_t{};
@@ -192,7 +200,7 @@ __device__ __forceinline__ void dq_block(
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       // S^T, dP^T for keys kb + 32 s .. + 31 (rows) x this wave's 32 queries (columns).
-      f32x16_t st = {}, dpt = {};
+      f32x16_t st = {}, dpt = DROPOUT ? f32x16_t{} : neg_d;
       __builtin_amdgcn_s_setprio(0);
       // The reads of step c + kPF are issued before the matrix instructions of
       // step c (the fences keep the scheduler from sinking them to their use).
@@ -238,9 +246,11 @@ __device__ __forceinline__ void dq_block(
         } else {
           p = fast_exp2(fmaf(st[r], zs, nl2));
         }
-        float dp = dpt[r];
-        if (DROPOUT) dp = keep.keep(r, drop.keep_t) ? dp * drop.scale : 0.f;
-        float ds = p * (dp - dval);
+        // dP - D: the accumulator holds it already without dropout; with
+        // dropout the mask and 1/(1-p) apply to dP alone.
+        float dpd = dpt[r];
+        if (DROPOUT) dpd = (keep.keep(r, drop.keep_t) ? dpd * drop.scale : 0.f) - dval;
+        float ds = p * dpd;
         if (SOFTCAP) ds *= dt;
         st[r] = ds;
       }
