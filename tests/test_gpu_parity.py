@@ -76,6 +76,20 @@ def test_long_sequence_sampled_heads():
             assert e <= TOL[w.dtype]
 
 
+def test_one_head_share_full_oracle():
+    """One head at N = 16384 (256 work units: the combined dK/dV + dQ launch at
+    full length), every output against the oracle."""
+    w = workloads.WORKLOADS["bf16_causal_b1h1_n16384_d128"]
+    x = workloads.make_inputs(w)
+    got = run_gpu(w, x)
+    print(f"[{w.name}] kernels done; oracle", flush=True)
+    ref = oracle_kv_heads(w, x, 0, [0])
+    for n in ("O", "LSE", "D", "dQ", "dK", "dV"):
+        e = rel_err(to_np(got[n][0, 0]), ref[n][0])
+        print(f"[{w.name}] {n}={e:.2e}", flush=True)
+        assert e <= TOL[w.dtype], n
+
+
 @pytest.mark.parametrize("cap,drop", [(0.0, None), (10.0, (0.1, 77, 2))], ids=["plain", "softcap_dropout"])
 def test_standalone_kernels_d64(cap, drop):
     """B=8 H=8 N=2048 d=64 causal: 1024 dK/dV and 1024 dQ work units, more than
