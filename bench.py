@@ -1,8 +1,8 @@
 """Benchmark of the attention backward hot path on one MI355X.
 
-One step = attn_bwd_preprocess (D = rowsum(dO o O), dQaccum <- 0) + attn_bwd +
-attn_bwd_dq_convert on the long-sequence causal workload (B=1, H=8, N=16384,
-d=128, bf16), with Q, K, V, dO, O and LSE resident in HBM before the timed
+One step = attn_bwd_preprocess (D = rowsum(dO o O)) + attn_bwd_with_dq (dK, dV
+and dQ = scale * sum_j dS K_j rounded to bf16) on the long-sequence causal
+workload (B=1, H=8, N=16384, d=128, bf16), with Q, K, V, dO, O and LSE resident in HBM before the timed
 region (O and LSE come from attn_fwd_stats, outside the timed region).
 
 Throughput: backward FLOPs of the metric, 10 N^2 d per query head, halved for
@@ -56,7 +56,7 @@ def source_sha(paths):
 
 
 def measured_traffic(workload, launch_bytes_key="bytes_per_launch"):
-    """HBM bytes per attn_bwd launch from committed rocprofv3 counter runs,
+    """HBM bytes per attn_bwd_with_dq launch from committed rocprofv3 counter runs,
     valid only for the workload they were taken on and while the kernel
     source is the one they were taken on."""
     try:
@@ -156,18 +156,15 @@ def main():
         fab.attn_bwd_preprocess(o, do, D, acc, H_kv=w.H_kv, **kw)
         if ev is not None:
             ev[1].record()
-        fab.attn_bwd(q, k, v, do, lse, D, acc, dk, dv, dropout=w.dropout, **kw)
+        fab.attn_bwd_with_dq(q, k, v, do, lse, D, acc, dq, dk, dv, dropout=w.dropout, **kw)
         if ev is not None:
             ev[2].record()
-        fab.attn_bwd_dq_convert(acc, dq, scale=w.tau)
-        if ev is not None:
-            ev[3].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     # Timed region: exactly K steps, synchronised on both sides.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -176,7 +173,6 @@ def main():
     wall = time.perf_counter() - t0
     pre = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     bwd = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    cvt = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
 
     # Cold caches: before each of these steps a 512 MiB fill (twice the
     # 256 MB Infinity Cache, far above the L2s) evicts the inputs; only the
@@ -184,12 +180,12 @@ def main():
     cold = None
     if args.cold_steps > 0:
         flush = torch.empty(1 << 27, device=dev, dtype=torch.float32)
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.cold_steps)]
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.cold_steps)]
         for i in range(args.cold_steps):
             flush.fill_(float(i))
             step(cev[i])
         torch.cuda.synchronize()
-        cms = sorted(e[0].elapsed_time(e[3]) for e in cev)[args.cold_steps // 2]
+        cms = sorted(e[0].elapsed_time(e[2]) for e in cev)[args.cold_steps // 2]
         cold = {"ms_per_step": round(cms, 4), "tflops": round(w.flops() / (cms * 1e-3) / 1e12, 2),
                 "steps": args.cold_steps, "statistic": "median of event-timed steps, each after a 512 MiB fill"}
         del flush
@@ -211,7 +207,6 @@ def main():
     bwd_tflops = flops / (bwd * 1e-3) / 1e12
     esz = 2 if w.dtype == "bf16" else 4
     pre_bytes = 2 * B * H * N * d * esz + B * H * N * 4           # read O, dO; write D
-    cvt_bytes = B * H * N * d * 4 + B * H * N * d * esz           # read dQaccum; write dQ
     traffic = measured_traffic(w.name)
     out = {
         "metric": METRIC,
@@ -232,15 +227,14 @@ def main():
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(bwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "attn_bwd entry point (bf16: bwd_dkdv_kernel + bwd_dq_kernel)",
+                     "kernel": "attn_bwd_with_dq entry point (bf16: bwd_dkdv_kernel + bwd_dq_kernel, "
+                               "which writes dQ)",
                      "flops_per_launch": flops,
                      "note": "achieved = metric FLOPs (10 N^2 d per head, halved when causal; with a local window "
-                             "10 d per visible (query, key) pair) / measured attn_bwd time; the two kernels issue "
+                             "10 d per visible (query, key) pair) / measured attn_bwd_with_dq time; the two kernels issue "
                              "14/10 of that as MFMA work because the dQ kernel recomputes S and dP"},
-        "kernels_ms": {"bwd_preprocess": round(pre, 4), "bwd": round(bwd, 4), "bwd_dq_convert": round(cvt, 4)},
-        "stream_kernels_GBs": {"bwd_preprocess": round(pre_bytes / (pre * 1e-3) / 1e9, 1),
-                               "bwd_dq_convert": round(cvt_bytes / (cvt * 1e-3) / 1e9, 1),
-                               "peak": PEAK_HBM_GBS},
+        "kernels_ms": {"bwd_preprocess": round(pre, 4), "bwd_with_dq": round(bwd, 4)},
+        "stream_kernels_GBs": {"bwd_preprocess": round(pre_bytes / (pre * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS},
         "cold_cache": cold,
         "forward": {"kernel": "attn_fwd_stats (not part of the timed step)", "ms": round(fwd_ms, 4),
                     "tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 1), "flops": "4/10 of the backward metric FLOPs"},

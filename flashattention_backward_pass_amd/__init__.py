@@ -1,7 +1,8 @@
 """MI355X (gfx950) FlashAttention backward: Python binding of libfabwd.so.
 
 The functions named like the C entry points (``attn_fwd_stats``,
-``attn_bwd_preprocess``, ``attn_bwd``, ``attn_bwd_dq_convert``) only marshal
+``attn_bwd_preprocess``, ``attn_bwd``, ``attn_bwd_dq_convert``,
+``attn_bwd_with_dq``) only marshal
 arguments: they read shapes and device pointers from torch tensors, pass the
 current HIP stream, and raise on a non-zero status.  Every step of the
 computation runs in the library's kernels.  The library is loaded on first
@@ -29,6 +30,7 @@ EXPORTS = {
     "attn_bwd_preprocess": [_P, _P, _P, _P, _P, _P],
     "attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "attn_bwd_dq_convert": [_P, _P, _P, _P],
+    "attn_bwd_with_dq": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "attn_status_str": [ctypes.c_int],
     "attn_version": [],
 }
@@ -186,9 +188,7 @@ def attn_bwd_preprocess(o, do, D, dq_accum, *, H_kv=None, causal=False, scale=No
            "attn_bwd_preprocess")
 
 
-def attn_bwd(q, k, v, do, lse, D, dq_accum, dk, dv, *, causal=False, scale=None, softcap=0.0, stream=None,
-             deterministic=False, window=None, dropout=None):
-    p = _params_from(q, k, causal, scale, softcap, deterministic, window, dropout)
+def _expect_bwd(q, k, v, do, lse, D, dq_accum, dk, dv):
     f32 = _torch().float32
     _expect(v, k.shape, q.dtype, "V")
     _expect(do, q.shape, q.dtype, "dO")
@@ -197,9 +197,25 @@ def attn_bwd(q, k, v, do, lse, D, dq_accum, dk, dv, *, causal=False, scale=None,
     _expect(dq_accum, q.shape, f32, "dQaccum")
     _expect(dk, k.shape, q.dtype, "dK")
     _expect(dv, k.shape, q.dtype, "dV")
+
+
+def attn_bwd(q, k, v, do, lse, D, dq_accum, dk, dv, *, causal=False, scale=None, softcap=0.0, stream=None,
+             deterministic=False, window=None, dropout=None):
+    p = _params_from(q, k, causal, scale, softcap, deterministic, window, dropout)
+    _expect_bwd(q, k, v, do, lse, D, dq_accum, dk, dv)
     lib = load_library()
     _check(lib.attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D),
                         _ptr(dq_accum), _ptr(dk), _ptr(dv), _stream(stream)), "attn_bwd")
+
+
+def attn_bwd_with_dq(q, k, v, do, lse, D, dq_accum, dq, dk, dv, *, causal=False, scale=None, softcap=0.0,
+                     stream=None, deterministic=False, window=None, dropout=None):
+    p = _params_from(q, k, causal, scale, softcap, deterministic, window, dropout)
+    _expect_bwd(q, k, v, do, lse, D, dq_accum, dk, dv)
+    _expect(dq, q.shape, q.dtype, "dQ")
+    lib = load_library()
+    _check(lib.attn_bwd_with_dq(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D),
+                                _ptr(dq_accum), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)), "attn_bwd_with_dq")
 
 
 def attn_bwd_dq_convert(dq_accum, dq, *, scale=None, stream=None):
@@ -224,7 +240,7 @@ def attention_forward(q, k, v, *, causal=False, scale=None, softcap=0.0, stream=
 
 def attention_backward(q, k, v, o, do, lse, *, causal=False, scale=None, softcap=0.0, stream=None,
                        workspace=None, deterministic=False, window=None, dropout=None):
-    """Returns (dQ, dK, dV): preprocess -> bwd -> dq_convert on one stream.
+    """Returns (dQ, dK, dV): preprocess -> bwd_with_dq on one stream.
 
     ``dropout`` = (p, seed, offset) must be what the forward used.
 
@@ -245,7 +261,6 @@ def attention_backward(q, k, v, o, do, lse, *, causal=False, scale=None, softcap
     dv = torch.empty_like(v)
     attn_bwd_preprocess(o, do, D, acc, H_kv=k.shape[1], causal=causal, scale=scale, softcap=softcap, stream=stream,
                         window=window)
-    attn_bwd(q, k, v, do, lse, D, acc, dk, dv, causal=causal, scale=scale, softcap=softcap, stream=stream,
-             deterministic=deterministic, window=window, dropout=dropout)
-    attn_bwd_dq_convert(acc, dq, scale=scale if scale is not None else d ** -0.5, stream=stream)
+    attn_bwd_with_dq(q, k, v, do, lse, D, acc, dq, dk, dv, causal=causal, scale=scale, softcap=softcap,
+                     stream=stream, deterministic=deterministic, window=window, dropout=dropout)
     return dq, dk, dv

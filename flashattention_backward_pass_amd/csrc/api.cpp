@@ -115,7 +115,18 @@ int attn_bwd(const attn_params* p, const void* Q, const void* K, const void* V, 
   if (rc != ATTN_OK || empty) return rc;
   if ((rc = check_ptrs({Q, K, V, dO, LSE, D, dQaccum, dK, dV})) != ATTN_OK) return rc;
   return finish(
-      fabwd::launch_bwd(pr, Q, K, V, dO, LSE, D, dQaccum, dK, dV, static_cast<hipStream_t>(stream)));
+      fabwd::launch_bwd(pr, Q, K, V, dO, LSE, D, dQaccum, dK, dV, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd_with_dq(const attn_params* p, const void* Q, const void* K, const void* V, const void* dO,
+                     const float* LSE, const float* D, float* dQaccum, void* dQ, void* dK, void* dV, void* stream) {
+  fabwd::Problem pr;
+  bool empty = false;
+  int rc = check_params(p, &pr, &empty);
+  if (rc != ATTN_OK || empty) return rc;
+  if ((rc = check_ptrs({Q, K, V, dO, LSE, D, dQaccum, dQ, dK, dV})) != ATTN_OK) return rc;
+  return finish(
+      fabwd::launch_bwd(pr, Q, K, V, dO, LSE, D, dQaccum, dK, dV, dQ, static_cast<hipStream_t>(stream)));
 }
 
 int attn_bwd_dq_convert(const attn_params* p, const float* dQaccum, void* dQ, void* stream) {

@@ -48,8 +48,8 @@ template <int D, bool SOFTCAP, bool DROPOUT>
 __device__ __forceinline__ void dq_block(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    float* __restrict__ dQacc, int H, int H_kv, int N, int BHq, float scale, float softcap, int wl, int wr,
-    Dropout drop, unsigned block) {
+    float* __restrict__ dQacc, bf16_t* __restrict__ dQout, int H, int H_kv, int N, int BHq, float scale,
+    float softcap, int wl, int wr, Dropout drop, unsigned block) {
   constexpr int KC = D / 16;
   constexpr int NT = D / 32;
   // Double buffers as separate variables: the compiler gives each LDS
@@ -291,13 +291,27 @@ __device__ __forceinline__ void dq_block(
     if (step + 1 < s_hi) body(B1{}, step + 1);
   }
 
-  // dQaccum rows of this wave (unscaled).  Register r: row 32w + 8(r/4) + 4g + r%4.
+  // Rows of this wave, register r: row 32w + 8(r/4) + 4g + r%4.  Either
+  // dQaccum (unscaled fp32) or, given dQout, dQ itself: the same fp32 product
+  // scale * acc and round-to-nearest-even as the convert kernel, so the bits
+  // equal those of the two-step path.
+  if (dQout) {
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
+    for (int n = 0; n < NT; ++n) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int q = q0 + 32 * w + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (q < N) dQacc[(q_off + q) * D + 32 * n + l32] = dq_acc[n][r];
+      for (int r = 0; r < 16; ++r) {
+        const int q = q0 + 32 * w + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (q < N) dQout[(q_off + q) * D + 32 * n + l32].bits = f32_to_bf16(scale * dq_acc[n][r]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = q0 + 32 * w + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (q < N) dQacc[(q_off + q) * D + 32 * n + l32] = dq_acc[n][r];
+      }
     }
   }
 }

@@ -28,7 +28,8 @@ template <int D, bool SOFTCAP, bool DROPOUT>
 __global__ __launch_bounds__(kThreads, 1) void bwd_fused_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, float* __restrict__ dQacc, int H, int H_kv, int N,
+    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, float* __restrict__ dQacc, bf16_t* __restrict__ dQout, int H,
+    int H_kv, int N,
     int BH_kv, int BH_q, float scale, float softcap, int wl, int wr, Dropout drop, unsigned n_dkdv, unsigned n_dq) {
   // Blocks 0 .. 2m-1 alternate between the two kinds (m = the smaller
   // count); the rest belong to the larger kind.
@@ -44,8 +45,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_fused_kernel(
     unit = b - m;
   }
   if (dq_unit)
-    dq::dq_block<D, SOFTCAP, DROPOUT>(Q, K, V, dO, LSE, Dv, dQacc, H, H_kv, N, BH_q, scale, softcap, wl, wr, drop,
-                                      unit);
+    dq::dq_block<D, SOFTCAP, DROPOUT>(Q, K, V, dO, LSE, Dv, dQacc, dQout, H, H_kv, N, BH_q, scale, softcap, wl, wr,
+                                      drop, unit);
   else
     dkdv::dkdv_block<D, SOFTCAP, DROPOUT>(Q, K, V, dO, LSE, Dv, dK, dV, H, H_kv, N, BH_kv, scale, softcap, wl, wr,
                                           1, nullptr, drop, unit);
@@ -58,24 +59,24 @@ unsigned dq_units(const Problem& p) { return unsigned(p.B * p.H) * unsigned((p.N
 
 template <int D, bool SOFTCAP, bool DROPOUT>
 hipError_t fused_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                   const float* Dv, void* dK, void* dV, float* dQacc, hipStream_t s) {
+                   const float* Dv, void* dK, void* dV, float* dQacc, void* dQout, hipStream_t s) {
   const unsigned n1 = dkdv_units(p), n2 = dq_units(p);
   hipLaunchKernelGGL((bwd_fused_kernel<D, SOFTCAP, DROPOUT>), dim3(n1 + n2), dim3(kThreads), 0, s,
                      static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V),
                      static_cast<const bf16_t*>(dO), LSE, Dv, static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV),
-                     dQacc, p.H, p.H_kv, p.N, p.B * p.H_kv, p.B * p.H, p.scale, p.softcap, p.wl, p.wr, p.drop(), n1,
+                     dQacc, static_cast<bf16_t*>(dQout), p.H, p.H_kv, p.N, p.B * p.H_kv, p.B * p.H, p.scale, p.softcap, p.wl, p.wr, p.drop(), n1,
                      n2);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t fused_d(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                   const float* Dv, void* dK, void* dV, float* dQacc, hipStream_t s) {
+                   const float* Dv, void* dK, void* dV, float* dQacc, void* dQout, hipStream_t s) {
   if (p.dropout)
-    return p.softcap > 0.f ? fused_t<D, true, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, dQacc, s)
-                           : fused_t<D, false, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, dQacc, s);
-  return p.softcap > 0.f ? fused_t<D, true, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, dQacc, s)
-                         : fused_t<D, false, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, dQacc, s);
+    return p.softcap > 0.f ? fused_t<D, true, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, dQacc, dQout, s)
+                           : fused_t<D, false, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, dQacc, dQout, s);
+  return p.softcap > 0.f ? fused_t<D, true, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, dQacc, dQout, s)
+                         : fused_t<D, false, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, dQacc, dQout, s);
 }
 
 }  // namespace
@@ -87,10 +88,10 @@ bool bwd_fused_fits(const Problem& p) {
 
 hipError_t launch_bwd_fused_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                                  const float* LSE, const float* Dv, void* dK, void* dV, float* dQacc,
-                                 hipStream_t s) {
+                                 void* dQout, hipStream_t s) {
   if (!bwd_fused_fits(p)) return hipErrorInvalidValue;
-  return p.d == 64 ? fused_d<64>(p, Q, K, V, dO, LSE, Dv, dK, dV, dQacc, s)
-                   : fused_d<128>(p, Q, K, V, dO, LSE, Dv, dK, dV, dQacc, s);
+  return p.d == 64 ? fused_d<64>(p, Q, K, V, dO, LSE, Dv, dK, dV, dQacc, dQout, s)
+                   : fused_d<128>(p, Q, K, V, dO, LSE, Dv, dK, dV, dQacc, dQout, s);
 }
 
 }  // namespace fabwd

@@ -12,23 +12,27 @@ hipError_t launch_fwd_stats(const Problem& p, const void* Q, const void* K, cons
 }
 
 hipError_t launch_bwd(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
-                      const float* LSE, const float* D, float* dQacc, void* dK, void* dV, hipStream_t s) {
+                      const float* LSE, const float* D, float* dQacc, void* dK, void* dV, void* dQ,
+                      hipStream_t s) {
   (void)hipGetLastError();
   // bf16: matrix-core kernels; fp32: vector-ALU kernel (same fp32 peak on MI355X).
   if (p.dtype == 1) {
     // Few work units: both kinds in one launch, so that they share the chip.
-    if (bwd_fused_fits(p)) return launch_bwd_fused_mfma(p, Q, K, V, dO, LSE, D, dK, dV, dQacc, s);
-    // dQaccum is overwritten by the dQ kernel afterwards: until then the
-    // dK/dV kernel may keep partial sums in it.
+    // Given dQ, the dQ work units write it directly (the same bits as
+    // dq_convert of their dQaccum rows).
+    if (bwd_fused_fits(p)) return launch_bwd_fused_mfma(p, Q, K, V, dO, LSE, D, dK, dV, dQacc, dQ, s);
+    // dQaccum is overwritten by the dQ kernel afterwards (or no longer
+    // needed): until then the dK/dV kernel may keep partial sums in it.
     hipError_t e = launch_bwd_dkdv_mfma(p, Q, K, V, dO, LSE, D, dK, dV, dQacc, s);
     if (e != hipSuccess) return e;
-    return launch_bwd_dq_mfma(p, Q, K, V, dO, LSE, D, dQacc, s);
+    return launch_bwd_dq_mfma(p, Q, K, V, dO, LSE, D, dQacc, dQ, s);
   }
   // fp32: dQ partials added with atomics (the pages' scheme), or, in
   // deterministic mode, dK/dV alone plus a query-block-outer dQ kernel.
   hipError_t e = launch_bwd_simple(p, Q, K, V, dO, LSE, D, dQacc, dK, dV, s);
-  if (e != hipSuccess || !p.deterministic) return e;
-  return launch_bwd_dq_simple(p, Q, K, V, dO, LSE, D, dQacc, s);
+  if (e == hipSuccess && p.deterministic) e = launch_bwd_dq_simple(p, Q, K, V, dO, LSE, D, dQacc, s);
+  if (e != hipSuccess || !dQ) return e;
+  return launch_bwd_dq_convert(p, dQacc, dQ, s);
 }
 
 }  // namespace fabwd

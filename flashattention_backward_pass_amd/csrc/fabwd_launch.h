@@ -36,8 +36,11 @@ hipError_t launch_fwd_stats(const Problem& p, const void* Q, const void* K, cons
                             hipStream_t s);
 hipError_t launch_bwd_preprocess(const Problem& p, const void* O, const void* dO, float* D, float* dQacc,
                                  hipStream_t s);
+// dQ (dtype) non-null: dQ = scale * dQaccum is written as well (bf16: by
+// the dQ kernel itself, and dQaccum is then only scratch).
 hipError_t launch_bwd(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
-                      const float* LSE, const float* D, float* dQacc, void* dK, void* dV, hipStream_t s);
+                      const float* LSE, const float* D, float* dQacc, void* dK, void* dV, void* dQ,
+                      hipStream_t s);
 hipError_t launch_bwd_dq_convert(const Problem& p, const float* dQacc, void* dQ, hipStream_t s);
 
 // Kernel families behind launch_fwd_stats / launch_bwd (dispatch.cpp picks
@@ -53,14 +56,15 @@ hipError_t launch_bwd_simple(const Problem& p, const void* Q, const void* K, con
 hipError_t launch_bwd_dq_simple(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                                 const float* LSE, const float* Dv, float* dQacc, hipStream_t s);
 // bf16 matrix-core backward: dK/dV kernel (key blocks outer) and dQ kernel
-// (query blocks outer); the dQ kernel overwrites dQaccum.
+// (query blocks outer); the dQ kernel overwrites dQaccum, or, given dQout,
+// writes dQ = scale * acc in bf16 instead and leaves dQaccum alone.
 // scratch: B*H*N*d floats the kernel may use for partial sums before the
 // dQ kernel overwrites them (dQaccum), or nullptr.
 hipError_t launch_bwd_dkdv_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                                 const float* LSE, const float* Dv, void* dK, void* dV, float* scratch,
                                 hipStream_t s);
 hipError_t launch_bwd_dq_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
-                              const float* LSE, const float* D, float* dQacc, hipStream_t s);
+                              const float* LSE, const float* D, float* dQacc, void* dQout, hipStream_t s);
 // Workgroups sharing each (b, kv head, key block) unit of the dK/dV kernel:
 // 2 for grouped heads (G >= 4) with few units, whose fp32 partials then use
 // the scratch space (dQaccum) before the dQ kernel overwrites it; else 1.
@@ -70,6 +74,7 @@ int dkdv_split_count(const Problem& p, bool have_scratch);
 // dkdv_split_count(p, true) == 1.
 bool bwd_fused_fits(const Problem& p);
 hipError_t launch_bwd_fused_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
-                                 const float* LSE, const float* D, void* dK, void* dV, float* dQacc, hipStream_t s);
+                                 const float* LSE, const float* D, void* dK, void* dV, float* dQacc, void* dQout,
+                                 hipStream_t s);
 
 }  // namespace fabwd

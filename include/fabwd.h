@@ -164,6 +164,26 @@ int attn_bwd(const attn_params* p, const void* Q, const void* K, const void* V,
  */
 int attn_bwd_dq_convert(const attn_params* p, const float* dQaccum, void* dQ, void* stream);
 
+/*
+ * attn_bwd_with_dq - attn_bwd and attn_bwd_dq_convert in one call: dK, dV
+ * and dQ = scale * sum_j dS_ij K_j ([FA1] eqs (15), (16) with the scale of
+ * eq (7)) in dtype, [B, H, N, d] row-major, overwritten.  dQ gets the same
+ * bits as attn_bwd followed by attn_bwd_dq_convert.
+ *   bf16: the query-block-outer dQ work units round their fp32 sums and
+ *         store dQ directly (no convert launch, no fp32 dQ round trip);
+ *         dQaccum is still required as scratch (the grouped-head split of
+ *         the dK/dV work keeps partial sums there) and its contents are
+ *         unspecified afterwards.
+ *   fp32: attn_bwd, then the convert kernel; dQaccum holds the unscaled
+ *         sums afterwards, as with attn_bwd.
+ * dQ must not overlap any other buffer.  Inputs, D (from
+ * attn_bwd_preprocess on the same stream), errors and the deterministic
+ * flag as for attn_bwd.
+ */
+int attn_bwd_with_dq(const attn_params* p, const void* Q, const void* K, const void* V,
+                     const void* dO, const float* LSE, const float* D,
+                     float* dQaccum, void* dQ, void* dK, void* dV, void* stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* attn_status_str(int status);
 

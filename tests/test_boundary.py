@@ -79,7 +79,11 @@ def call_all(lib, p, ptr=A):
         lib.attn_bwd_preprocess(pp, ptr, ptr, ptr, ptr, S),
         lib.attn_bwd(pp, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, S),
         lib.attn_bwd_dq_convert(pp, ptr, ptr, S),
+        lib.attn_bwd_with_dq(pp, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, S),
     ]
+
+
+N_ENTRY = 5  # entry points that call_all exercises
 
 
 BAD = [
@@ -98,23 +102,23 @@ def test_invalid_arguments(lib, bad):
               window_left=-1, window_right=-1, dropout_p=0.0, rng_seed_lo=0, rng_seed_hi=0, rng_offset=0)
     kw.update(bad)
     p = fab.attn_params(**kw)
-    assert call_all(lib, p) == [fab.ATTN_ERR_INVALID_ARG] * 4
+    assert call_all(lib, p) == [fab.ATTN_ERR_INVALID_ARG] * N_ENTRY
 
 
 @pytest.mark.parametrize("d", [32, 96, 256])
 def test_unsupported_head_dim(lib, d):
-    assert call_all(lib, fab.make_params(1, 2, 2, 64, d, 1)) == [fab.ATTN_ERR_UNSUPPORTED] * 4
+    assert call_all(lib, fab.make_params(1, 2, 2, 64, d, 1)) == [fab.ATTN_ERR_UNSUPPORTED] * N_ENTRY
 
 
 @pytest.mark.parametrize("det", [2, -1])
 def test_deterministic_flag_out_of_range(lib, det):
-    assert call_all(lib, fab.make_params(1, 2, 2, 64, 64, 1, deterministic=det)) == [fab.ATTN_ERR_INVALID_ARG] * 4
+    assert call_all(lib, fab.make_params(1, 2, 2, 64, 64, 1, deterministic=det)) == [fab.ATTN_ERR_INVALID_ARG] * N_ENTRY
 
 
 @pytest.mark.parametrize("dtype", [0, 1])
 def test_deterministic_mode_accepted(lib, dtype):
     # An empty problem validates every argument but launches nothing.
-    assert call_all(lib, fab.make_params(1, 2, 2, 0, 64, dtype, deterministic=1), ptr=None) == [fab.ATTN_OK] * 4
+    assert call_all(lib, fab.make_params(1, 2, 2, 0, 64, dtype, deterministic=1), ptr=None) == [fab.ATTN_OK] * N_ENTRY
 
 
 def test_null_params(lib):
@@ -123,42 +127,42 @@ def test_null_params(lib):
 
 def test_null_pointers(lib):
     assert call_all(lib, fab.make_params(1, 2, 2, 64, 64, 1), ptr=ctypes.c_void_p(0)) == \
-        [fab.ATTN_ERR_INVALID_ARG] * 4
+        [fab.ATTN_ERR_INVALID_ARG] * N_ENTRY
 
 
 def test_misaligned_pointers(lib):
-    assert call_all(lib, fab.make_params(1, 2, 2, 64, 64, 1), ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * 4
+    assert call_all(lib, fab.make_params(1, 2, 2, 64, 64, 1), ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * N_ENTRY
 
 
 def test_too_many_elements(lib):
-    assert call_all(lib, fab.make_params(1 << 12, 1 << 10, 1, 1 << 13, 128, 1)) == [fab.ATTN_ERR_INVALID_ARG] * 4
+    assert call_all(lib, fab.make_params(1 << 12, 1 << 10, 1, 1 << 13, 128, 1)) == [fab.ATTN_ERR_INVALID_ARG] * N_ENTRY
     # B*H*N*d just above 2^36 is rejected; exactly 2^36 passes the size check, so
     # those calls fail on the (null or misaligned) pointers instead.
     over = fab.make_params(1, 1 << 9, 1 << 9, (1 << 20) + 1, 128, 1)
-    assert call_all(lib, over) == [fab.ATTN_ERR_INVALID_ARG] * 4
+    assert call_all(lib, over) == [fab.ATTN_ERR_INVALID_ARG] * N_ENTRY
     at = fab.make_params(1, 1 << 9, 1 << 9, 1 << 20, 128, 1)
-    assert call_all(lib, at, ptr=ctypes.c_void_p(0)) == [fab.ATTN_ERR_INVALID_ARG] * 4  # null pointers
-    assert call_all(lib, at, ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * 4  # size accepted, pointer checked next
+    assert call_all(lib, at, ptr=ctypes.c_void_p(0)) == [fab.ATTN_ERR_INVALID_ARG] * N_ENTRY  # null pointers
+    assert call_all(lib, at, ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * N_ENTRY  # size accepted, pointer checked next
 
 
 def test_grid_limits(lib):
     """Short sequences with very many heads: few elements, but a grid of
     2*B*H*ceil(N/128) workgroups of 256 work-items past 2^32 is rejected."""
     many = fab.make_params(1 << 22, 4, 4, 1, 64, 1)  # 2^30 elements, 2^33 work-items
-    assert call_all(lib, many) == [fab.ATTN_ERR_INVALID_ARG] * 4
+    assert call_all(lib, many) == [fab.ATTN_ERR_INVALID_ARG] * N_ENTRY
     fits = fab.make_params(1 << 20, 4, 4, 1, 64, 1)  # 2^31 work-items: size accepted, pointers checked
-    assert call_all(lib, fits, ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * 4
+    assert call_all(lib, fits, ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * N_ENTRY
     # fp32 puts B and H in the second and third grid dimensions
-    assert call_all(lib, fab.make_params(65536, 1, 1, 16, 64, 0), ptr=MIS) == [fab.ATTN_ERR_INVALID_ARG] * 4
-    assert call_all(lib, fab.make_params(65535, 1, 1, 16, 64, 0), ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * 4
-    assert call_all(lib, fab.make_params(65536, 1, 1, 16, 64, 1), ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * 4
+    assert call_all(lib, fab.make_params(65536, 1, 1, 16, 64, 0), ptr=MIS) == [fab.ATTN_ERR_INVALID_ARG] * N_ENTRY
+    assert call_all(lib, fab.make_params(65535, 1, 1, 16, 64, 0), ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * N_ENTRY
+    assert call_all(lib, fab.make_params(65536, 1, 1, 16, 64, 1), ptr=MIS) == [fab.ATTN_ERR_MISALIGNED] * N_ENTRY
 
 
 @pytest.mark.parametrize("shape", [(0, 2, 2, 64), (1, 2, 2, 0)])
 def test_empty_problems_are_ok_without_pointers(lib, shape):
     B, H, Hkv, N = shape
     assert call_all(lib, fab.make_params(B, H, Hkv, N, 128, 1, causal=1), ptr=ctypes.c_void_p(0)) == \
-        [fab.ATTN_OK] * 4
+        [fab.ATTN_OK] * N_ENTRY
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
@@ -209,20 +213,23 @@ def test_binding_checks_buffers_of_the_other_entry_points():
         fab.attn_bwd_preprocess(t["o"], t["do"], short, t["acc"], H_kv=2)
     with pytest.raises(ValueError, match="dQaccum"):
         fab.attn_bwd_dq_convert(t["acc"][:, :, :7], t["dq"])
+    with pytest.raises(ValueError, match="dQ"):
+        fab.attn_bwd_with_dq(t["q"], t["k"], t["v"], t["do"], t["lse"], t["D"], t["acc"], t["dq"][:, :, :7],
+                             t["dk"], t["dv"])
 
 
 @pytest.mark.parametrize("window", [(0, 0), (5, -1), (-1, 3), (1 << 24, 7)])
 def test_windows_accepted(lib, window):
     # Valid windows on an empty problem: every argument is checked, nothing runs.
     p = fab.make_params(1, 2, 2, 0, 64, 1, causal=1, window=window)
-    assert call_all(lib, p, ptr=None) == [fab.ATTN_OK] * 4
+    assert call_all(lib, p, ptr=None) == [fab.ATTN_OK] * N_ENTRY
 
 
 @pytest.mark.parametrize("p", [0.0, 0.1, 0.999])
 def test_dropout_accepted(lib, p):
     params = fab.make_params(1, 2, 2, 0, 64, 1, dropout=(p, (1 << 64) - 1, (1 << 32) - 1))
     assert (params.rng_seed_lo, params.rng_seed_hi, params.rng_offset) == (0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF)
-    assert call_all(lib, params, ptr=None) == [fab.ATTN_OK] * 4
+    assert call_all(lib, params, ptr=None) == [fab.ATTN_OK] * N_ENTRY
 
 
 def test_dropout_seed_range():
