@@ -1,4 +1,5 @@
-"""The backward step (preprocess, bwd, dq_convert) captured in a HIP graph.
+"""The backward step (preprocess, bwd, dq_convert, or preprocess and
+bwd_with_dq) captured in a HIP graph.
 
 The library only enqueues kernels on the caller's stream (no memsets, no
 allocations, no synchronisation), so a captured step must replay to the
@@ -25,8 +26,9 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("with_dq", [False, True], ids=["three_calls", "with_dq"])
 @pytest.mark.parametrize("case", CASES, ids=["bf16", "bf16_two_kernels", "bf16_gqa_dropout", "fp32_det", "fp32_atomic"])
-def test_graph_replays_match_eager(case):
+def test_graph_replays_match_eager(case, with_dq):
     B, H, Hkv, N, d, dt, causal, drop, det = case
     w = workloads.custom(B, H, Hkv, N, d, dt, causal, 0.0, seed=N + H, name="graph", dropout=drop)
     x = workloads.make_inputs(w)
@@ -40,8 +42,11 @@ def test_graph_replays_match_eager(case):
 
     def step():
         fab.attn_bwd_preprocess(o, do, D, acc, H_kv=Hkv, causal=causal, scale=w.tau)
-        fab.attn_bwd(q, k, v, do, lse, D, acc, dk, dv, deterministic=det, **kw)
-        fab.attn_bwd_dq_convert(acc, dq, scale=w.tau)
+        if with_dq:
+            fab.attn_bwd_with_dq(q, k, v, do, lse, D, acc, dq, dk, dv, deterministic=det, **kw)
+        else:
+            fab.attn_bwd(q, k, v, do, lse, D, acc, dk, dv, deterministic=det, **kw)
+            fab.attn_bwd_dq_convert(acc, dq, scale=w.tau)
 
     step()
     torch.cuda.synchronize()
