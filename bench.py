@@ -33,6 +33,7 @@ DEFAULT_WORKLOAD = "bf16_causal_b1h8_n16384_d128"
 BWD_SOURCES = [os.path.join(ROOT, "flashattention_backward_pass_amd", "csrc", f)
                for f in ("bwd_dkdv.hip", "bwd_dkdv_block.h", "bwd_dq.hip", "bwd_dq_block.h", "mfma_common.h", "philox.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "bwd_mfma.json")
 
 
 def parse():
@@ -66,6 +67,18 @@ def measured_traffic(workload, launch_bytes_key="bytes_per_launch"):
     if t.get("workload") != workload or t.get("source_sha") != source_sha(BWD_SOURCES):
         return None
     return t.get(launch_bytes_key)
+
+
+def measured_mfma(workload):
+    """MFMA instructions per attn_bwd_with_dq launch (SQ_INSTS_MFMA of a
+    committed rocprofv3 run), under the same validity rule as the traffic."""
+    try:
+        t = json.load(open(MFMA_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("source_sha") != source_sha(BWD_SOURCES):
+        return None
+    return sum(t["mfma_per_launch"].values()), t["flop_per_mfma"]
 
 
 def copy_calibration(torch):
@@ -208,6 +221,15 @@ def main():
     esz = 2 if w.dtype == "bf16" else 4
     pre_bytes = 2 * B * H * N * d * esz + B * H * N * 4           # read O, dO; write D
     traffic = measured_traffic(w.name)
+    mfma = measured_mfma(w.name)
+    mfma_issue = None
+    if mfma is not None:
+        issued = mfma[0] * mfma[1] / (bwd * 1e-3) / 1e12
+        mfma_issue = {"instructions_per_launch": mfma[0], "tflops": round(issued, 2),
+                      "frac_of_peak": round(issued / PEAK_BF16_TFLOPS, 4),
+                      "note": "matrix work the kernels issue (S and dP are computed twice, once per kernel; "
+                              "diagonal tiles in full) per measured attn_bwd_with_dq time, against the same peak; "
+                              "instruction count from profiles/bwd_mfma.json"}
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -229,7 +251,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "attn_bwd_with_dq entry point (bf16: bwd_dkdv_kernel + bwd_dq_kernel, "
                                "which writes dQ)",
-                     "flops_per_launch": flops,
+                     "flops_per_launch": flops, "mfma_issue": mfma_issue,
                      "note": "achieved = metric FLOPs (10 N^2 d per head, halved when causal; with a local window "
                              "10 d per visible (query, key) pair) / measured attn_bwd_with_dq time; the two kernels issue "
                              "14/10 of that as MFMA work because the dQ kernel recomputes S and dP"},
