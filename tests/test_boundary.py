@@ -237,3 +237,17 @@ def test_dropout_seed_range():
         fab.make_params(1, 2, 2, 8, 64, 1, dropout=(0.1, 1 << 64, 0))
     with pytest.raises(ValueError):
         fab.make_params(1, 2, 2, 8, 64, 1, dropout=(0.1, 0, 1 << 32))
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/fabwd.h compiles as C99 with -pedantic (a C-ABI header: no C++ or torch types)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not installed")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    src = tmp_path / "use_header.c"
+    src.write_text('#include "fabwd.h"\nint main(void) { attn_params p; (void)p; return 0; }\n')
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", inc, str(src),
+                        "-o", str(tmp_path / "use_header")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
