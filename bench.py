@@ -99,7 +99,9 @@ def copy_calibration(torch):
 
 def cpu_baseline(w, x, heads=3):
     """The fp64 oracle, untuned, on the first `heads` query heads of batch 0 of
-    the workload at full N (about 4 s of host time per head at N = 16384)."""
+    the workload at full N.  Each head's forward (O, LSE: the backward's
+    inputs) runs first, untimed apart; the backward alone is timed, and its
+    rate is the metric FLOPs of those heads over the backward time."""
     import numpy as np
     import oracle
     try:
@@ -109,19 +111,25 @@ def cpu_baseline(w, x, heads=3):
         blas_threads = 1
     heads = min(heads, w.H)
     group = w.H // w.H_kv
-    t0 = time.perf_counter()
+    t_fwd = t_bwd = 0.0
     for h in range(heads):
         q, do = x["Q"][0, h], x["dO"][0, h]
         k, v = x["K"][0, h // group], x["V"][0, h // group]
         zf = oracle.head_dropout(w.dropout, h)
+        t0 = time.perf_counter()
         O, L = oracle.forward_head(q, k, v, w.tau, w.causal, w.softcap, w.window, zf)
+        t1 = time.perf_counter()
         oracle.backward_head(q, k, v, O, do, L, w.tau, w.causal, w.softcap, w.window, zf)
-    dt = time.perf_counter() - t0
+        t2 = time.perf_counter()
+        t_fwd += t1 - t0
+        t_bwd += t2 - t1
     flops = heads * w.flops() / (w.B * w.H)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"{heads} query heads (b=0, h=0..{heads - 1}) of the workload at full N={w.N}: "
-                      f"fp64 forward + backward, {dt:.1f} s wall; metric FLOPs of those heads",
-            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+    return {"value": flops / t_bwd / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{heads} query heads (b=0, h=0..{heads - 1}) of the workload at full N={w.N}: fp64 "
+                      f"backward alone, {t_bwd:.1f} s wall (their forward, {t_fwd:.1f} s, timed apart); "
+                      f"metric FLOPs of those heads",
+            "seconds": round(t_bwd, 3), "forward_seconds": round(t_fwd, 3),
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
 
 
 def cpu_model():
@@ -203,6 +211,21 @@ def main():
                 "steps": args.cold_steps, "statistic": "median of event-timed steps, each after a 512 MiB fill"}
         del flush
 
+    # attn_bwd_dq_convert (dQ = scale * dQaccum in bf16), which the timed
+    # step does not need (attn_bwd_with_dq stores dQ itself): timed on its own
+    # over the same tensors, with events on the launch stream.
+    conv_iters = 20
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    dq_conv = torch.empty_like(q)
+    fab.attn_bwd_dq_convert(acc, dq_conv, scale=w.tau)
+    ce[0].record()
+    for _ in range(conv_iters):
+        fab.attn_bwd_dq_convert(acc, dq_conv, scale=w.tau)
+    ce[1].record()
+    torch.cuda.synchronize()
+    conv_ms = ce[0].elapsed_time(ce[1]) / conv_iters
+    del dq_conv
+
     # The forward (attn_fwd_stats) is a support step outside the timed
     # backward step; timed here on its own for reference.
     fe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -220,6 +243,7 @@ def main():
     bwd_tflops = flops / (bwd * 1e-3) / 1e12
     esz = 2 if w.dtype == "bf16" else 4
     pre_bytes = 2 * B * H * N * d * esz + B * H * N * 4           # read O, dO; write D
+    conv_bytes = B * H * N * d * (4 + esz)                         # read dQaccum; write dQ
     traffic = measured_traffic(w.name)
     mfma = measured_mfma(w.name)
     mfma_issue = None
@@ -256,7 +280,14 @@ def main():
                              "10 d per visible (query, key) pair) / measured attn_bwd_with_dq time; the two kernels issue "
                              "14/10 of that as MFMA work because the dQ kernel recomputes S and dP"},
         "kernels_ms": {"bwd_preprocess": round(pre, 4), "bwd_with_dq": round(bwd, 4)},
-        "stream_kernels_GBs": {"bwd_preprocess": round(pre_bytes / (pre * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS},
+        "stream_kernels_GBs": {"bwd_preprocess": round(pre_bytes / (pre * 1e-3) / 1e9, 1),
+                               "bwd_dq_convert": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1),
+                               "peak": PEAK_HBM_GBS,
+                               "bytes": {"bwd_preprocess": pre_bytes, "bwd_dq_convert": conv_bytes},
+                               "ms": {"bwd_preprocess": round(pre, 5), "bwd_dq_convert": round(conv_ms, 5)},
+                               "note": "algorithmic bytes (preprocess: read O, dO, write D; convert: read "
+                                       "dQaccum, write dQ) / event-timed duration; convert is timed apart "
+                                       f"({conv_iters} back-to-back launches), the step does not run it"},
         "cold_cache": cold,
         "forward": {"kernel": "attn_fwd_stats (not part of the timed step)", "ms": round(fwd_ms, 4),
                     "tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 1), "flops": "4/10 of the backward metric FLOPs"},

@@ -112,7 +112,11 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
   const int bh = unit % BH, split = unit / BH;
   const int jblk = block / (BH * n_split);
   const int b = bh / H_kv, hk = bh % H_kv;
-  const int G = H / H_kv / n_split;  // query heads of this workgroup
+  // Query heads [g_lo, g_hi) of the group (of G_full = H / H_kv) belong to
+  // this workgroup; with an odd group the later split takes one head more.
+  const int G_full = H / H_kv;
+  const int g_lo = split * G_full / n_split, g_hi = (split + 1) * G_full / n_split;
+  const int G = g_hi - g_lo;  // query heads of this workgroup
   const int k0 = jblk * BC;
   const int64_t kv_off = (int64_t(b) * H_kv + hk) * N;  // row offset of this kv head
   const int kw = w * 32;                                 // this wave's first key in the block
@@ -160,7 +164,7 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
   // query blocks from the last one down (concurrent workgroups of a head sweep
   // the same rows together).  A cursor steps through that sequence without
   // divisions; one cursor feeds the copies, one the compute.
-  const int64_t head0 = (int64_t(b) * H + (hk * n_split + split) * G) * N;
+  const int64_t head0 = (int64_t(b) * H + hk * G_full + g_lo) * N;
   auto advance = [&](Cursor& c) {
     if (c.q0 == i_lo * BR) {
       c.q0 = q_last;
@@ -460,7 +464,7 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
     }
     __syncthreads();
   }
-  Cursor cc{q_last, head0, int(b) * H + (hk * n_split + split) * G};  // tile being computed
+  Cursor cc{q_last, head0, int(b) * H + hk * G_full + g_lo};  // tile being computed
   Cursor ci = cc;            // tile being copied
   {
 #pragma unroll

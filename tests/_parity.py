@@ -25,8 +25,12 @@ def to_np(t):
     return t.detach().double().cpu().numpy()
 
 
-def run_gpu(w, x, *, o=None, lse=None, poison=False, deterministic=False):
-    """Forward (unless o/lse given) then backward on cuda:0.  Returns numpy dict."""
+def run_gpu(w, x, *, o=None, lse=None, poison=False, deterministic=False, with_dq=False):
+    """Forward (unless o/lse given) then backward on cuda:0.  Returns a dict of
+    device tensors.  with_dq=False: attn_bwd_preprocess, attn_bwd and
+    attn_bwd_dq_convert (the four-call interface); with_dq=True:
+    attn_bwd_preprocess and attn_bwd_with_dq, the step the benchmark times
+    (dQaccum is then scratch and is not returned)."""
     dev = torch.device("cuda:0")
     q, k, v, do = (x[n].to(dev) for n in ("Q", "K", "V", "dO"))
     if o is None:
@@ -43,6 +47,11 @@ def run_gpu(w, x, *, o=None, lse=None, poison=False, deterministic=False):
             t.fill_(float("nan"))
     fab.attn_bwd_preprocess(o, do, D, acc, H_kv=w.H_kv, causal=w.causal, scale=w.tau, softcap=w.softcap,
                             window=w.window)
+    if with_dq:
+        fab.attn_bwd_with_dq(q, k, v, do, lse, D, acc, dq, dk, dv, causal=w.causal, scale=w.tau,
+                             softcap=w.softcap, deterministic=deterministic, window=w.window, dropout=w.dropout)
+        torch.cuda.synchronize()
+        return {"O": o, "LSE": lse, "D": D, "dQ": dq, "dK": dk, "dV": dv}
     fab.attn_bwd(q, k, v, do, lse, D, acc, dk, dv, causal=w.causal, scale=w.tau, softcap=w.softcap,
                  deterministic=deterministic, window=w.window, dropout=w.dropout)
     acc_copy = acc.clone()
@@ -51,15 +60,33 @@ def run_gpu(w, x, *, o=None, lse=None, poison=False, deterministic=False):
     return {"O": o, "LSE": lse, "D": D, "dQaccum": acc_copy, "dQ": dq, "dK": dk, "dV": dv}
 
 
+_ORACLE_CACHE = {}
+
+
 def oracle_full(w, x):
+    """The full oracle of a workload (inputs are the seeded ones of make_inputs(w));
+    the last two workloads' results are kept, so tests that check two paths of
+    one workload compute it once."""
+    if w in _ORACLE_CACHE:
+        return _ORACLE_CACHE[w]
+    r = _oracle_full(w, x)
+    while len(_ORACLE_CACHE) >= 2:
+        _ORACLE_CACHE.pop(next(iter(_ORACLE_CACHE)))
+    _ORACLE_CACHE[w] = r
+    return r
+
+
+def _oracle_full(w, x):
     return oracle.reference(x["Q"], x["K"], x["V"], x["dO"], w.tau, w.causal, w.softcap, w.window, w.dropout)
 
 
-def oracle_kv_heads(w, x, b, kv_heads):
+def oracle_kv_heads(w, x, b, kv_heads, progress=False):
     """Full per-head oracle for batch b and the given key/value heads (all their query heads)."""
     G = w.group
     out = {"O": {}, "LSE": {}, "D": {}, "dQ": {}, "dK": {}, "dV": {}}
     for g in kv_heads:
+        if progress:
+            print(f"[{w.name}] oracle b{b} kv head {g}", flush=True)
         k, v = x["K"][b, g], x["V"][b, g]
         dk = dv = 0.0
         for h in range(g * G, (g + 1) * G):

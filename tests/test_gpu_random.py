@@ -4,7 +4,7 @@ Each case draws head dim, grouped-head ratio, batch, a ragged or tiny N, the
 causal flag, a local window, the soft cap, dropout and the dtype together,
 so that combinations the hand-picked cases do not name run through the C ABI
 (the small grids take the combined dK/dV + dQ launch, grouped heads with
-G >= 4 the head split).  Same tolerance as the other parity tests:
+G >= 4 the head split, odd groups included).  Same tolerance as the other parity tests:
 max|GPU - oracle| / max|oracle| per output tensor.
 
 Where every query row sees exactly one key (N = 1, or a window that keeps
@@ -31,7 +31,7 @@ def _cases(n=24, seed=20261202):
     out = []
     for _ in range(n):
         d = rng.choice([64, 128])
-        G = rng.choice([1, 1, 2, 4])
+        G = rng.choice([1, 1, 2, 3, 4, 5, 7])
         Hkv = rng.choice([1, 2])
         B = rng.choice([1, 2])
         N = rng.choice([1, 7, 63, 64, 65, 127, 129, 200, 255, 300, 383])

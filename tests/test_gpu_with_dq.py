@@ -22,12 +22,14 @@ CASES = [
     # B, H, H_kv, N, d, dtype, causal, softcap, window, dropout, deterministic
     (1, 4, 4, 700, 128, "bf16", True, 0.0, (-1, -1), None, False),             # combined launch, ragged
     (4, 16, 16, 1100, 64, "bf16", True, 0.0, (-1, -1), None, False),           # two kernels (> 1024 workgroups)
+    (2, 16, 16, 2100, 128, "bf16", True, 0.0, (-1, -1), None, False),          # two kernels, d = 128, ragged
+    (1, 20, 4, 700, 128, "bf16", True, 0.0, (-1, -1), None, False),            # head split, G = 5
     (1, 8, 2, 900, 128, "bf16", True, 0.0, (-1, -1), (0.2, 99, 4), False),     # head split, dropout
     (2, 4, 2, 333, 128, "bf16", False, 15.0, (40, 20), None, False),          # soft cap, window
     (1, 2, 2, 200, 64, "fp32", True, 0.0, (-1, -1), None, True),              # fp32, fixed order
     (1, 2, 1, 257, 128, "fp32", False, 5.0, (-1, -1), None, False),            # fp32, atomics
 ]
-IDS = ["bf16_combined", "bf16_two_kernels", "bf16_split_dropout", "bf16_softcap_window", "fp32_det", "fp32_atomic"]
+IDS = ["bf16_combined", "bf16_two_kernels", "bf16_two_kernels_d128", "bf16_split_g5", "bf16_split_dropout", "bf16_softcap_window", "fp32_det", "fp32_atomic"]
 
 
 @pytest.mark.parametrize("case", CASES, ids=IDS)
