@@ -211,19 +211,26 @@ def main():
                 "steps": args.cold_steps, "statistic": "median of event-timed steps, each after a 512 MiB fill"}
         del flush
 
-    # attn_bwd_dq_convert (dQ = scale * dQaccum in bf16), which the timed
-    # step does not need (attn_bwd_with_dq stores dQ itself): timed on its own
-    # over the same tensors, with events on the launch stream.
-    conv_iters = 20
-    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    # The two bandwidth-bound kernels, each timed over back-to-back launches
+    # (kernel throughput; the per-step time of the preprocess above also holds
+    # the launch gap after the previous step).  attn_bwd_dq_convert (dQ = scale
+    # * dQaccum in bf16) is not part of the step (attn_bwd_with_dq stores dQ
+    # itself); it runs over the same tensors.
+    stream_iters = 20
     dq_conv = torch.empty_like(q)
-    fab.attn_bwd_dq_convert(acc, dq_conv, scale=w.tau)
-    ce[0].record()
-    for _ in range(conv_iters):
-        fab.attn_bwd_dq_convert(acc, dq_conv, scale=w.tau)
-    ce[1].record()
-    torch.cuda.synchronize()
-    conv_ms = ce[0].elapsed_time(ce[1]) / conv_iters
+
+    def back_to_back(fn):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(stream_iters):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / stream_iters
+
+    pre_b2b = back_to_back(lambda: fab.attn_bwd_preprocess(o, do, D, acc, H_kv=w.H_kv, **kw))
+    conv_ms = back_to_back(lambda: fab.attn_bwd_dq_convert(acc, dq_conv, scale=w.tau))
     del dq_conv
 
     # The forward (attn_fwd_stats) is a support step outside the timed
@@ -280,14 +287,19 @@ def main():
                              "10 d per visible (query, key) pair) / measured attn_bwd_with_dq time; the two kernels issue "
                              "14/10 of that as MFMA work because the dQ kernel recomputes S and dP"},
         "kernels_ms": {"bwd_preprocess": round(pre, 4), "bwd_with_dq": round(bwd, 4)},
-        "stream_kernels_GBs": {"bwd_preprocess": round(pre_bytes / (pre * 1e-3) / 1e9, 1),
+        "stream_kernels_GBs": {"bwd_preprocess": round(pre_bytes / (pre_b2b * 1e-3) / 1e9, 1),
                                "bwd_dq_convert": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1),
                                "peak": PEAK_HBM_GBS,
+                               "frac_of_peak": {"bwd_preprocess": round(pre_bytes / (pre_b2b * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                                "bwd_dq_convert": round(conv_bytes / (conv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
                                "bytes": {"bwd_preprocess": pre_bytes, "bwd_dq_convert": conv_bytes},
-                               "ms": {"bwd_preprocess": round(pre, 5), "bwd_dq_convert": round(conv_ms, 5)},
+                               "ms": {"bwd_preprocess": round(pre_b2b, 5), "bwd_dq_convert": round(conv_ms, 5)},
+                               "bwd_preprocess_in_step_ms": round(pre, 5),
                                "note": "algorithmic bytes (preprocess: read O, dO, write D; convert: read "
-                                       "dQaccum, write dQ) / event-timed duration; convert is timed apart "
-                                       f"({conv_iters} back-to-back launches), the step does not run it"},
+                                       f"dQaccum, write dQ) / duration over {stream_iters} back-to-back launches "
+                                       "(events on the launch stream); bwd_preprocess_in_step_ms is the event time "
+                                       "of the step's own preprocess call, launch gap included; the step does not "
+                                       "run convert"},
         "cold_cache": cold,
         "forward": {"kernel": "attn_fwd_stats (not part of the timed step)", "ms": round(fwd_ms, 4),
                     "tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 1), "flops": "4/10 of the backward metric FLOPs"},

@@ -31,6 +31,7 @@ EXPORTS = {
     "attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "attn_bwd_dq_convert": [_P, _P, _P, _P],
     "attn_bwd_with_dq": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "attn_bwd_kernels": [_P, ctypes.c_int],
     "attn_status_str": [ctypes.c_int],
     "attn_version": [],
 }
@@ -81,7 +82,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name, args in EXPORTS.items():
         fn = getattr(lib, name)
         fn.argtypes = args
-        fn.restype = ctypes.c_char_p if name in ("attn_status_str", "attn_version") else ctypes.c_int
+        fn.restype = ctypes.c_char_p if name in ("attn_status_str", "attn_version", "attn_bwd_kernels") else ctypes.c_int
     _lib = lib
     return lib
 
@@ -161,6 +162,17 @@ def _expect(t, shape, dtype, name):
 def _check(status: int, where: str):
     if status != ATTN_OK:
         raise AttnError(status, where)
+
+
+def attn_bwd_kernels(q, k, *, causal=False, scale=None, softcap=0.0, deterministic=False, window=None,
+                     dropout=None, with_dq=True) -> str:
+    """Kernel names (launch order, '+'-separated) that attn_bwd_with_dq (with_dq=True) or attn_bwd
+    runs for these shapes on the current device."""
+    p = _params_from(q, k, causal, scale, softcap, deterministic, window, dropout)
+    r = load_library().attn_bwd_kernels(ctypes.byref(p), int(bool(with_dq)))
+    if r is None:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "attn_bwd_kernels")
+    return r.decode()
 
 
 def attn_fwd_stats(q, k, v, o, lse, *, causal=False, scale=None, softcap=0.0, stream=None, window=None,

@@ -104,5 +104,24 @@ def _check_kernel_stubs(lib: str) -> None:
         raise RuntimeError("kernel launch stubs missing from libfabwd.so: " + ", ".join(missing))
 
 
+PROBE_SRC = os.path.join(PKG, "probes", "dq_update_probe.cpp")
+PROBE_BIN = os.path.join(BUILD, "dq_update_probe")
+
+
+def build_probe() -> str:
+    """Builds the standalone dQ-update traffic probe (probes/dq_update_probe.cpp)
+    into _build/dq_update_probe; run it directly (or under rocprofv3)."""
+    os.makedirs(BUILD, exist_ok=True)
+    cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", PROBE_SRC, "-o", PROBE_BIN]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"build of the dQ-update probe failed:\n{r.stdout}{r.stderr}")
+    return PROBE_BIN
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--probe" in sys.argv:
+        print(build_probe())
+    else:
+        print(build(verbose="-v" in sys.argv))

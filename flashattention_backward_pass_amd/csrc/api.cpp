@@ -138,6 +138,14 @@ int attn_bwd_dq_convert(const attn_params* p, const float* dQaccum, void* dQ, vo
   return finish(fabwd::launch_bwd_dq_convert(pr, dQaccum, dQ, static_cast<hipStream_t>(stream)));
 }
 
+const char* attn_bwd_kernels(const attn_params* p, int with_dq) {
+  fabwd::Problem pr;
+  bool empty = false;
+  if (check_params(p, &pr, &empty) != ATTN_OK || (with_dq != 0 && with_dq != 1)) return nullptr;
+  if (empty) return "";
+  return fabwd::bwd_kernels(pr, with_dq != 0);
+}
+
 const char* attn_status_str(int status) {
   switch (status) {
     case ATTN_OK: return "ATTN_OK";

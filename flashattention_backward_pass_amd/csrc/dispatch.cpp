@@ -11,6 +11,18 @@ hipError_t launch_fwd_stats(const Problem& p, const void* Q, const void* K, cons
   return launch_fwd_simple(p, Q, K, V, O, LSE, s);
 }
 
+const char* bwd_kernels(const Problem& p, bool with_dq) {
+  if (p.dtype == 1) {
+    if (bwd_fused_fits(p)) return "bwd_fused_kernel";
+    return dkdv_split_count(p, true) > 1 ? "bwd_dkdv_kernel+dkdv_split_sum_kernel+bwd_dq_kernel"
+                                         : "bwd_dkdv_kernel+bwd_dq_kernel";
+  }
+  if (p.deterministic)
+    return with_dq ? "bwd_simple_kernel+bwd_dq_simple_kernel+dq_convert_kernel"
+                   : "bwd_simple_kernel+bwd_dq_simple_kernel";
+  return with_dq ? "bwd_simple_kernel+dq_convert_kernel" : "bwd_simple_kernel";
+}
+
 hipError_t launch_bwd(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                       const float* LSE, const float* D, float* dQacc, void* dK, void* dV, void* dQ,
                       hipStream_t s) {

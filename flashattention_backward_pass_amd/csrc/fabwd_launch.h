@@ -42,6 +42,9 @@ hipError_t launch_bwd(const Problem& p, const void* Q, const void* K, const void
                       const float* LSE, const float* D, float* dQacc, void* dK, void* dV, void* dQ,
                       hipStream_t s);
 hipError_t launch_bwd_dq_convert(const Problem& p, const float* dQacc, void* dQ, hipStream_t s);
+// Names of the kernels launch_bwd runs for p (with or without dQ), in launch
+// order, '+'-separated (static strings; the same decisions as launch_bwd).
+const char* bwd_kernels(const Problem& p, bool with_dq);
 
 // Kernel families behind launch_fwd_stats / launch_bwd (dispatch.cpp picks
 // one): the *_simple launchers are the fp32 vector kernels (fp32 only; they

