@@ -31,6 +31,7 @@ EXPORTS = {
     "attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "attn_bwd_dq_convert": [_P, _P, _P, _P],
     "attn_bwd_with_dq": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "attn_bwd_with_dq_noalloc": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "attn_bwd_kernels": [_P, ctypes.c_int],
     "attn_status_str": [ctypes.c_int],
     "attn_version": [],
@@ -228,6 +229,23 @@ def attn_bwd_with_dq(q, k, v, do, lse, D, dq_accum, dq, dk, dv, *, causal=False,
     lib = load_library()
     _check(lib.attn_bwd_with_dq(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D),
                                 _ptr(dq_accum), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)), "attn_bwd_with_dq")
+
+
+def attn_bwd_with_dq_noalloc(q, k, v, o, do, lse, dq, dk, dv, *, causal=False, scale=None, softcap=0.0,
+                             stream=None, deterministic=False, window=None, dropout=None):
+    """preprocess + attn_bwd_with_dq with the library's own static scratch (no allocation)."""
+    p = _params_from(q, k, causal, scale, softcap, deterministic, window, dropout)
+    f32 = _torch().float32
+    _expect(v, k.shape, q.dtype, "V")
+    _expect(o, q.shape, q.dtype, "O")
+    _expect(do, q.shape, q.dtype, "dO")
+    _expect(lse, q.shape[:3], f32, "LSE")
+    _expect(dq, q.shape, q.dtype, "dQ")
+    _expect(dk, k.shape, q.dtype, "dK")
+    _expect(dv, k.shape, q.dtype, "dV")
+    lib = load_library()
+    _check(lib.attn_bwd_with_dq_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                        _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)), "attn_bwd_with_dq_noalloc")
 
 
 def attn_bwd_dq_convert(dq_accum, dq, *, scale=None, stream=None):

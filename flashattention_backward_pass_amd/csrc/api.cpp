@@ -138,6 +138,17 @@ int attn_bwd_dq_convert(const attn_params* p, const float* dQaccum, void* dQ, vo
   return finish(fabwd::launch_bwd_dq_convert(pr, dQaccum, dQ, static_cast<hipStream_t>(stream)));
 }
 
+int attn_bwd_with_dq_noalloc(const attn_params* p, const void* Q, const void* K, const void* V, const void* O,
+                             const void* dO, const float* LSE, void* dQ, void* dK, void* dV, void* stream) {
+  fabwd::Problem pr;
+  bool empty = false;
+  int rc = check_params(p, &pr, &empty);
+  if (rc != ATTN_OK || empty) return rc;
+  if (fabwd::noalloc_scratch_floats(pr) > fabwd::noalloc_scratch_capacity()) return ATTN_ERR_INVALID_ARG;
+  if ((rc = check_ptrs({Q, K, V, O, dO, LSE, dQ, dK, dV})) != ATTN_OK) return rc;
+  return finish(fabwd::launch_bwd_noalloc(pr, Q, K, V, O, dO, LSE, dQ, dK, dV, static_cast<hipStream_t>(stream)));
+}
+
 const char* attn_bwd_kernels(const attn_params* p, int with_dq) {
   fabwd::Problem pr;
   bool empty = false;

@@ -42,6 +42,13 @@ hipError_t launch_bwd(const Problem& p, const void* Q, const void* K, const void
                       const float* LSE, const float* D, float* dQacc, void* dK, void* dV, void* dQ,
                       hipStream_t s);
 hipError_t launch_bwd_dq_convert(const Problem& p, const float* dQacc, void* dQ, hipStream_t s);
+// The allocation-free step (noalloc.cpp): preprocess + backward with every
+// scratch buffer in the library's own device array.  noalloc_scratch_floats:
+// what p needs; noalloc_scratch_capacity: what the array holds.
+int64_t noalloc_scratch_floats(const Problem& p);
+int64_t noalloc_scratch_capacity();
+hipError_t launch_bwd_noalloc(const Problem& p, const void* Q, const void* K, const void* V, const void* O,
+                              const void* dO, const float* LSE, void* dQ, void* dK, void* dV, hipStream_t s);
 // Names of the kernels launch_bwd runs for p (with or without dQ), in launch
 // order, '+'-separated (static strings; the same decisions as launch_bwd).
 const char* bwd_kernels(const Problem& p, bool with_dq);

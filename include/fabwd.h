@@ -185,6 +185,26 @@ int attn_bwd_with_dq(const attn_params* p, const void* Q, const void* K, const v
                      float* dQaccum, void* dQ, void* dK, void* dV, void* stream);
 
 /*
+ * attn_bwd_with_dq_noalloc - the whole backward step, attn_bwd_preprocess
+ * followed by attn_bwd_with_dq, with no caller-provided scratch and no
+ * allocation of any kind: for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Inputs Q, K, V, O, dO, LSE and outputs dQ, dK, dV as for
+ * attn_bwd_with_dq (same layouts, dtype and overwrite semantics; the results
+ * equal those of attn_bwd_preprocess + attn_bwd_with_dq on the same inputs).
+ * D and every scratch buffer of the step (fp32: the dQaccum sums; bf16 with
+ * the grouped-head split: the dK/dV partial sums) live in one static device
+ * array of 64 MiB that the library holds on each device it runs on until the
+ * process ends; calls that overlap on one device share it and race.
+ * Errors: as attn_bwd_with_dq, plus ATTN_ERR_INVALID_ARG when the step needs
+ * more than 2^24 floats of scratch: B*H*N (D) plus, for fp32, B*H*N*d, or,
+ * for bf16 when H / H_kv >= 4 and B*H_kv*ceil(N/128) < 1024, 4*B*H_kv*N*d.
+ */
+int attn_bwd_with_dq_noalloc(const attn_params* p, const void* Q, const void* K, const void* V,
+                             const void* O, const void* dO, const float* LSE,
+                             void* dQ, void* dK, void* dV, void* stream);
+
+/*
  * attn_bwd_kernels - the kernels that attn_bwd (with_dq = 0) or
  * attn_bwd_with_dq (with_dq = 1) launches for these parameters on the
  * current device, in launch order, separated by '+' (static storage; ""

@@ -271,3 +271,16 @@ def test_bwd_kernels_query(lib):
     assert plan(1, 8, 8, 16384, 128, fab.ATTN_BF16, 1) == b"bwd_dkdv_kernel+bwd_dq_kernel"
     assert plan(1, 32, 8, 1024, 128, fab.ATTN_BF16, 1) == b"bwd_dkdv_kernel+dkdv_split_sum_kernel+bwd_dq_kernel"
     assert plan(4, 16, 16, 4096, 64, fab.ATTN_BF16, 1, with_dq=0) == b"bwd_dkdv_kernel+bwd_dq_kernel"
+
+
+def test_noalloc_rejects_oversized_scratch(lib):
+    """attn_bwd_with_dq_noalloc keeps D and its scratch in a 2^24-float static
+    array: a step that needs more (fp32: B*H*N*(d+1) floats) is refused before
+    any device call; invalid parameters are refused as by the other calls."""
+    ptr = ctypes.c_void_p(256)
+    p = fab.make_params(1, 16, 16, 8192, 128, fab.ATTN_FP32, True)
+    assert lib.attn_bwd_with_dq_noalloc(ctypes.byref(p), *(ptr,) * 9, None) == fab.ATTN_ERR_INVALID_ARG
+    p = fab.make_params(1, 3, 2, 100, 64, fab.ATTN_BF16, True)
+    assert lib.attn_bwd_with_dq_noalloc(ctypes.byref(p), *(ptr,) * 9, None) == fab.ATTN_ERR_INVALID_ARG
+    p = fab.make_params(0, 2, 2, 100, 64, fab.ATTN_BF16, True)
+    assert lib.attn_bwd_with_dq_noalloc(ctypes.byref(p), *(None,) * 9, None) == fab.ATTN_OK
