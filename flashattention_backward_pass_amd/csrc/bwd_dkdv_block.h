@@ -489,26 +489,42 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
   }
 
   // Epilogue: dK = -tau * dK_acc (the accumulator holds -dS^T Q), dV = dV_acc
-  // (rows = keys, lanes = d); with a head split, the raw fp32 accumulators
-  // go to `part` ([2][n_split][B*H_kv*N][D]: dK partials, then dV partials).
+  // (rows = keys, columns = d), staged through the idle Q/dO tiles so that the
+  // global writes are 16-byte row chunks.  With a head split the raw fp32
+  // accumulators go to `part` ([2][n_split][B*H_kv*N][D]: dK partials, then dV
+  // partials), one tensor at a time (a 128 x D fp32 tile fills both buffers).
+  // Rows past N are not written.
   const int64_t plane = int64_t(BH) * N * D;
   const float v_scale = DROPOUT ? drop.scale : 1.f;  // dV sums P o keep; Z = keep / (1 - p)
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = k0 + kw + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (key < N) {
-        const int64_t off = (kv_off + key) * D + 32 * n + l32;
-        if (n_split == 1) {
-          dK[off].bits = f32_to_bf16(dk_acc[n][r] * -scale);
-          dV[off].bits = f32_to_bf16(dv_acc[n][r] * v_scale);
-        } else {
-          part[split * plane + off] = dk_acc[n][r];
-          part[(n_split + split) * plane + off] = dv_acc[n][r] * v_scale;
-        }
-      }
-    }
+  const int valid = min(BC, N - k0);
+  // The last tile's copies (into the idle buffer) must land before the tiles are reused.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // every wave is done with the Q/dO tiles
+  if (n_split == 1) {
+    bf16_t* tk = reinterpret_cast<bf16_t*>(sQO0);  // BC x D bf16 = the size of one buffer
+    bf16_t* tv = reinterpret_cast<bf16_t*>(sQO1);
+    stage_acc<bf16_t, NT, D>(tk, kw, dk_acc, -scale, lane);
+    stage_acc<bf16_t, NT, D>(tv, kw, dv_acc, v_scale, lane);
+    __syncthreads();
+    stage_copy_rows<bf16_t, D, kThreads>(dK + (kv_off + k0) * D, tk, BC, valid, tid);
+    stage_copy_rows<bf16_t, D, kThreads>(dV + (kv_off + k0) * D, tv, BC, valid, tid);
+  } else {
+    // 128 x D fp32 = both buffers: rows 0-63 in buffer 0, rows 64-127 in buffer 1.
+    float* t0 = reinterpret_cast<float*>(sQO0);
+    float* t1 = reinterpret_cast<float*>(sQO1);
+    float* tw = w < 2 ? t0 : t1;
+    const int row0 = kw - (w < 2 ? 0 : BC / 2);
+    float* dst_k = part + split * plane + (kv_off + k0) * D;
+    float* dst_v = part + (n_split + split) * plane + (kv_off + k0) * D;
+    stage_acc<float, NT, D>(tw, row0, dk_acc, 1.f, lane);
+    __syncthreads();
+    stage_copy_rows<float, D, kThreads>(dst_k, t0, BC / 2, valid, tid);
+    stage_copy_rows<float, D, kThreads>(dst_k + (BC / 2) * D, t1, BC / 2, valid - BC / 2, tid);
+    __syncthreads();
+    stage_acc<float, NT, D>(tw, row0, dv_acc, v_scale, lane);
+    __syncthreads();
+    stage_copy_rows<float, D, kThreads>(dst_v, t0, BC / 2, valid, tid);
+    stage_copy_rows<float, D, kThreads>(dst_v + (BC / 2) * D, t1, BC / 2, valid - BC / 2, tid);
   }
 }
 

@@ -294,25 +294,25 @@ __device__ __forceinline__ void dq_block(
   // Rows of this wave, register r: row 32w + 8(r/4) + 4g + r%4.  Either
   // dQaccum (unscaled fp32) or, given dQout, dQ itself: the same fp32 product
   // scale * acc and round-to-nearest-even as the convert kernel, so the bits
-  // equal those of the two-step path.
+  // equal those of the two-step path.  Staged through the idle K/V tiles so
+  // that the global writes are 16-byte row chunks; rows past N are skipped.
+  const int valid = min(BQ, N - q0);
+  // The last tile's copies (into the idle buffer) must land before the tiles are reused.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // every wave is done with the K/V tiles
   if (dQout) {
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = q0 + 32 * w + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (q < N) dQout[(q_off + q) * D + 32 * n + l32].bits = f32_to_bf16(scale * dq_acc[n][r]);
-      }
-    }
+    bf16_t* t = reinterpret_cast<bf16_t*>(sKV0);  // BQ x D bf16 = one buffer
+    stage_acc<bf16_t, NT, D>(t, 32 * w, dq_acc, scale, lane);
+    __syncthreads();
+    stage_copy_rows<bf16_t, D, kThreads>(dQout + (q_off + q0) * D, t, BQ, valid, tid);
   } else {
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = q0 + 32 * w + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (q < N) dQacc[(q_off + q) * D + 32 * n + l32] = dq_acc[n][r];
-      }
-    }
+    // BQ x D fp32 = both buffers: rows 0-63 in buffer 0, rows 64-127 in buffer 1.
+    float* t0 = reinterpret_cast<float*>(sKV0);
+    float* t1 = reinterpret_cast<float*>(sKV1);
+    stage_acc<float, NT, D>(w < 2 ? t0 : t1, 32 * w - (w < 2 ? 0 : BQ / 2), dq_acc, 1.f, lane);
+    __syncthreads();
+    stage_copy_rows<float, D, kThreads>(dQacc + (q_off + q0) * D, t0, BQ / 2, valid, tid);
+    stage_copy_rows<float, D, kThreads>(dQacc + (q_off + q0 + BQ / 2) * D, t1, BQ / 2, valid - BQ / 2, tid);
   }
 }
 

@@ -91,3 +91,46 @@ __device__ __forceinline__ int swz_off(int row, int chunk, int sub) {
 }
 
 }  // namespace fabwd
+
+namespace fabwd {
+
+// Epilogue staging.  A wave's 32 x (32 NT) fp32 accumulator block (acc[n],
+// register r: row row0 + 8(r/4) + 4(lane/32) + r%4, column 32n + lane%32) is
+// scaled by `mul`, converted to T and written into a row-major LDS tile of
+// COLS elements per row; stage_copy_rows then moves whole rows to global
+// memory with 16-byte accesses (a 2-byte store per lane and element would
+// touch 64 scattered bytes per instruction).
+template <typename T, int NT, int COLS>
+__device__ __forceinline__ void stage_acc(T* tile, int row0, const f32x16_t* acc, float mul, int lane) {
+  const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = row0 + 8 * (r >> 2) + 4 * g + (r & 3);
+      const float v = acc[n][r] * mul;
+      if constexpr (sizeof(T) == 2) {
+        reinterpret_cast<uint16_t*>(tile)[row * COLS + 32 * n + l32] = __builtin_bit_cast(uint16_t, (__bf16)v);
+      } else {
+        reinterpret_cast<float*>(tile)[row * COLS + 32 * n + l32] = v;
+      }
+    }
+  }
+}
+
+// Rows [0, rows) of a row-major LDS tile of COLS elements of T per row go to
+// dst + row * COLS; rows at or past `valid` are skipped.  All NTHREADS
+// threads of the workgroup take part.
+template <typename T, int COLS, int NTHREADS>
+__device__ __forceinline__ void stage_copy_rows(T* __restrict__ dst, const T* tile, int rows, int valid, int tid) {
+  constexpr int kPerChunk = 16 / sizeof(T);
+  constexpr int kChunks = COLS / kPerChunk;  // 16-byte chunks per row
+  for (int i = tid; i < rows * kChunks; i += NTHREADS) {
+    const int row = i / kChunks, c = i % kChunks;
+    if (row < valid)
+      *reinterpret_cast<u32x4_t*>(dst + int64_t(row) * COLS + c * kPerChunk) =
+          *reinterpret_cast<const u32x4_t*>(tile + row * COLS + c * kPerChunk);
+  }
+}
+
+}  // namespace fabwd
