@@ -78,7 +78,8 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
                                            const float* __restrict__ LSE, const float* __restrict__ Dv,
                                            bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int H, int H_kv, int N,
                                            int BH, float scale, float softcap, int wl, int wr, int n_split,
-                                           float* __restrict__ part, Dropout drop, unsigned block) {
+                                           float* __restrict__ part, Dropout drop, unsigned block,
+                                           int qhalf = -1, int qblocks = 0) {
   constexpr int KC = D / 16;  // 16-wide k chunks over d
   constexpr int NT = D / 32;  // 32-wide column tiles over d
   // Double buffers as separate variables: the compiler gives each LDS
@@ -107,7 +108,12 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
   // Work unit: (batch*kv-head, key block, head subset).  Key blocks vary
   // slowest so that the heaviest causal blocks (small j) are dispatched first.
   // With n_split > 1 the G query heads of the group are shared out over
-  // n_split workgroups, which write fp32 partial sums to `part`.
+  // n_split workgroups, which write fp32 partial sums to `part`.  With
+  // qhalf >= 0 (combined launch, n_split == 1) the caller has
+  // decoded the unit: `block` is bh + BH * jblk and this workgroup takes half
+  // qhalf of the key block's query tiles (0: the later ones, 1: the earlier
+  // ones), writing fp32 partials for fused_partial_sum_kernel: tile
+  // (2 qhalf + tensor) * BH * qblocks + bh * qblocks + jblk of BC x D floats.
   const int unit = block % (BH * n_split);
   const int bh = unit % BH, split = unit / BH;
   const int jblk = block / (BH * n_split);
@@ -154,8 +160,13 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
   const float cap_zs = softcap * zs;
   // Query blocks [i_lo, i_hi) hold every row that sees a key of this block.
   const int k_end = min(k0 + BC, N);
-  const int i_lo = max(0, k0 - wr) / BR;
-  const int i_hi = (min(N, k_end + wl) + BR - 1) / BR;
+  int i_lo = max(0, k0 - wr) / BR;
+  int i_hi = (min(N, k_end + wl) + BR - 1) / BR;
+  if (qhalf >= 0) {
+    const int mid = (i_lo + i_hi + 1) / 2;
+    if (qhalf == 0) i_lo = mid;
+    else i_hi = mid;
+  }
   const int n_iter = (i_hi - i_lo) * G;
   const bool ragged_keys = k0 + BC > N;
   const int q_last = (i_hi - 1) * BR;  // first row of the last query block visited
@@ -466,7 +477,7 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
   }
   Cursor cc{q_last, head0, int(b) * H + hk * G_full + g_lo};  // tile being computed
   Cursor ci = cc;            // tile being copied
-  {
+  if (n_iter > 0) {
 #pragma unroll
     for (int k = 0; k < NDMA; ++k) copy_one(B0{}, ci, k);
     prescale(B0{});
@@ -500,7 +511,7 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
   // The last tile's copies (into the idle buffer) must land before the tiles are reused.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();  // every wave is done with the Q/dO tiles
-  if (n_split == 1) {
+  if (n_split == 1 && qhalf < 0) {
     bf16_t* tk = reinterpret_cast<bf16_t*>(sQO0);  // BC x D bf16 = the size of one buffer
     bf16_t* tv = reinterpret_cast<bf16_t*>(sQO1);
     stage_acc<bf16_t, NT, D>(tk, kw, dk_acc, -scale, lane);
@@ -514,8 +525,17 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
     float* t1 = reinterpret_cast<float*>(sQO1);
     float* tw = w < 2 ? t0 : t1;
     const int row0 = kw - (w < 2 ? 0 : BC / 2);
-    float* dst_k = part + split * plane + (kv_off + k0) * D;
-    float* dst_v = part + (n_split + split) * plane + (kv_off + k0) * D;
+    float* dst_k;
+    float* dst_v;
+    if (qhalf >= 0) {
+      const int64_t tiles = int64_t(BH) * qblocks;
+      const int64_t t = int64_t(bh) * qblocks + jblk;
+      dst_k = part + ((2 * qhalf) * tiles + t) * (BC * D);
+      dst_v = part + ((2 * qhalf + 1) * tiles + t) * (BC * D);
+    } else {
+      dst_k = part + split * plane + (kv_off + k0) * D;
+      dst_v = part + (n_split + split) * plane + (kv_off + k0) * D;
+    }
     stage_acc<float, NT, D>(tw, row0, dk_acc, 1.f, lane);
     __syncthreads();
     stage_copy_rows<float, D, kThreads>(dst_k, t0, BC / 2, valid, tid);

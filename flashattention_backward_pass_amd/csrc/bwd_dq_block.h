@@ -49,7 +49,8 @@ __device__ __forceinline__ void dq_block(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     float* __restrict__ dQacc, bf16_t* __restrict__ dQout, int H, int H_kv, int N, int BHq, float scale,
-    float softcap, int wl, int wr, Dropout drop, unsigned block) {
+    float softcap, int wl, int wr, Dropout drop, unsigned block, int khalf = -1, int qq = 0,
+    float* __restrict__ part = nullptr) {
   constexpr int KC = D / 16;
   constexpr int NT = D / 32;
   // Double buffers as separate variables: the compiler gives each LDS
@@ -146,9 +147,18 @@ __device__ __forceinline__ void dq_block(
   }
 
   // Key blocks [s_lo, s_hi) hold every key that some row of this block sees.
+  // With khalf >= 0 (combined launch) this workgroup takes half khalf of them
+  // (0: the later ones, 1: the earlier ones) and writes its unscaled fp32 sum
+  // as a partial tile, khalf * BHq * qq + bhq * qq + (n_qblk - 1 - iblk) of
+  // BQ x D floats in `part`, for the sum kernel that follows the launch.
   const int q_hi = min(q0 + BQ, N) - 1;  // last valid row
-  const int s_lo = max(0, q0 - wl) / BK;
-  const int s_hi = (min(N, q_hi + wr + 1) + BK - 1) / BK;
+  int s_lo = max(0, q0 - wl) / BK;
+  int s_hi = (min(N, q_hi + wr + 1) + BK - 1) / BK;
+  if (khalf >= 0) {
+    const int mid = (s_lo + s_hi + 1) / 2;
+    if (khalf == 0) s_lo = mid;
+    else s_hi = mid;
+  }
 
   // Per-lane byte offsets of the K/V block copies: slab I = s*4 + w covers
   // rows I*RPS ..; lane L fills physical chunk L % (D/8) of row I*RPS + L/(D/8),
@@ -300,7 +310,7 @@ __device__ __forceinline__ void dq_block(
   // The last tile's copies (into the idle buffer) must land before the tiles are reused.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();  // every wave is done with the K/V tiles
-  if (dQout) {
+  if (dQout && khalf < 0) {
     bf16_t* t = reinterpret_cast<bf16_t*>(sKV0);  // BQ x D bf16 = one buffer
     stage_acc<bf16_t, NT, D>(t, 32 * w, dq_acc, scale, lane);
     __syncthreads();
@@ -309,10 +319,12 @@ __device__ __forceinline__ void dq_block(
     // BQ x D fp32 = both buffers: rows 0-63 in buffer 0, rows 64-127 in buffer 1.
     float* t0 = reinterpret_cast<float*>(sKV0);
     float* t1 = reinterpret_cast<float*>(sKV1);
+    float* dst = dQacc + (q_off + q0) * D;
+    if (khalf >= 0) dst = part + ((int64_t(khalf) * BHq + bhq) * qq + (n_qblk - 1 - iblk)) * (BQ * D);
     stage_acc<float, NT, D>(w < 2 ? t0 : t1, 32 * w - (w < 2 ? 0 : BQ / 2), dq_acc, 1.f, lane);
     __syncthreads();
-    stage_copy_rows<float, D, kThreads>(dQacc + (q_off + q0) * D, t0, BQ / 2, valid, tid);
-    stage_copy_rows<float, D, kThreads>(dQacc + (q_off + q0 + BQ / 2) * D, t1, BQ / 2, valid - BQ / 2, tid);
+    stage_copy_rows<float, D, kThreads>(dst, t0, BQ / 2, valid, tid);
+    stage_copy_rows<float, D, kThreads>(dst + (BQ / 2) * D, t1, BQ / 2, valid - BQ / 2, tid);
   }
 }
 

@@ -13,7 +13,8 @@ hipError_t launch_fwd_stats(const Problem& p, const void* Q, const void* K, cons
 
 const char* bwd_kernels(const Problem& p, bool with_dq) {
   if (p.dtype == 1) {
-    if (bwd_fused_fits(p)) return "bwd_fused_kernel";
+    if (bwd_fused_fits(p))
+      return fused_split(p, with_dq).floats > 0 ? "bwd_fused_kernel+fused_partial_sum_kernel" : "bwd_fused_kernel";
     return dkdv_split_count(p, true) > 1 ? "bwd_dkdv_kernel+dkdv_split_sum_kernel+bwd_dq_kernel"
                                          : "bwd_dkdv_kernel+bwd_dq_kernel";
   }

@@ -5,7 +5,9 @@
 //   [B*H*N, B*H*N + extra)          fp32: dQaccum (B*H*N*d, zeroed by the
 //                                   preprocess kernel); bf16 with the grouped-
 //                                   head split: the dK/dV partials
-//                                   (4*B*H_kv*N*d); otherwise nothing.
+//                                   (4*B*H_kv*N*d); bf16 with split units in
+//                                   the combined launch: their partials (at
+//                                   most B*H*N*d); otherwise nothing.
 // Each device holds its own copy of the array until the process ends; its
 // device address is looked up once per device (hipGetSymbolAddress) and only
 // that address is handed to kernels.  Calls that overlap on one device share
@@ -49,7 +51,7 @@ int64_t noalloc_scratch_floats(const Problem& p) {
   const int64_t rows = int64_t(p.B) * p.H * p.N;
   if (p.dtype == 0) return rows + rows * p.d;
   if (dkdv_split_count(p, true) > 1) return rows + 4 * int64_t(p.B) * p.H_kv * p.N * p.d;
-  return rows;
+  return rows + fused_split(p, true).floats;
 }
 
 int64_t noalloc_scratch_capacity() { return kScratchFloats; }

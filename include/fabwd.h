@@ -168,12 +168,20 @@ int attn_bwd_dq_convert(const attn_params* p, const float* dQaccum, void* dQ, vo
  * attn_bwd_with_dq - attn_bwd and attn_bwd_dq_convert in one call: dK, dV
  * and dQ = scale * sum_j dS_ij K_j ([FA1] eqs (15), (16) with the scale of
  * eq (7)) in dtype, [B, H, N, d] row-major, overwritten.  dQ gets the same
- * bits as attn_bwd followed by attn_bwd_dq_convert.
+ * bits as attn_bwd followed by attn_bwd_dq_convert, and dK, dV those of
+ * attn_bwd, except for split units (below).
  *   bf16: the query-block-outer dQ work units round their fp32 sums and
  *         store dQ directly (no convert launch, no fp32 dQ round trip);
  *         dQaccum is still required as scratch (the grouped-head split of
  *         the dK/dV work keeps partial sums there) and its contents are
- *         unspecified afterwards.
+ *         unspecified afterwards.  Small causal or windowed problems whose
+ *         heaviest work units outweigh the rest take the combined launch
+ *         with those units split in two (dK/dV of the first key blocks by
+ *         query range, dQ of the last query blocks by key range), partial
+ *         sums in dQaccum (attn_bwd_kernels then names
+ *         fused_partial_sum_kernel): their rows add two fp32 halves before
+ *         rounding and may differ from attn_bwd's in the last bit; they are
+ *         still the same from run to run.
  *   fp32: attn_bwd, then the convert kernel; dQaccum holds the unscaled
  *         sums afterwards, as with attn_bwd.
  * dQ must not overlap any other buffer.  Inputs, D (from
@@ -198,7 +206,8 @@ int attn_bwd_with_dq(const attn_params* p, const void* Q, const void* K, const v
  * process ends; calls that overlap on one device share it and race.
  * Errors: as attn_bwd_with_dq, plus ATTN_ERR_INVALID_ARG when the step needs
  * more than 2^24 floats of scratch: B*H*N (D) plus, for fp32, B*H*N*d, or,
- * for bf16 when H / H_kv >= 4 and B*H_kv*ceil(N/128) < 1024, 4*B*H_kv*N*d.
+ * for bf16 when H / H_kv >= 4 and B*H_kv*ceil(N/128) < 1024, 4*B*H_kv*N*d,
+ * or, for bf16 with split units in the combined launch, at most B*H*N*d.
  */
 int attn_bwd_with_dq_noalloc(const attn_params* p, const void* Q, const void* K, const void* V,
                              const void* O, const void* dO, const float* LSE,

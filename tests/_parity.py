@@ -80,8 +80,20 @@ def _oracle_full(w, x):
     return oracle.reference(x["Q"], x["K"], x["V"], x["dO"], w.tau, w.causal, w.softcap, w.window, w.dropout)
 
 
+_KV_CACHE = {}
+
+
 def oracle_kv_heads(w, x, b, kv_heads, progress=False):
-    """Full per-head oracle for batch b and the given key/value heads (all their query heads)."""
+    """Full per-head oracle for batch b and the given key/value heads (all their
+    query heads); the last result is kept for a second path of the same heads."""
+    key = (w, b, tuple(kv_heads))
+    if key not in _KV_CACHE:
+        _KV_CACHE.clear()
+        _KV_CACHE[key] = _oracle_kv_heads(w, x, b, kv_heads, progress)
+    return _KV_CACHE[key]
+
+
+def _oracle_kv_heads(w, x, b, kv_heads, progress):
     G = w.group
     out = {"O": {}, "LSE": {}, "D": {}, "dQ": {}, "dK": {}, "dV": {}}
     for g in kv_heads:

@@ -268,6 +268,15 @@ def test_bwd_kernels_query(lib):
     assert plan(1, 2, 2, 100, 64, fab.ATTN_FP32, det=1, with_dq=0) == b"bwd_simple_kernel+bwd_dq_simple_kernel"
     assert plan(1, 4, 4, 512, 128, fab.ATTN_BF16, 1) == b"bwd_fused_kernel"
     assert plan(1, 4, 4, 512, 128, fab.ATTN_BF16, 1, with_dq=0) == b"bwd_fused_kernel"
+    # Given dQ, a combined launch whose heaviest causal units outweigh the
+    # per-compute-unit average splits them; balanced grids do not.
+    split = b"bwd_fused_kernel+fused_partial_sum_kernel"
+    assert plan(1, 1, 1, 16384, 128, fab.ATTN_BF16, 1) == split
+    assert plan(1, 1, 1, 16384, 128, fab.ATTN_BF16, 1, with_dq=0) == b"bwd_fused_kernel"
+    assert plan(1, 2, 1, 3000, 128, fab.ATTN_BF16, 1) == split
+    assert plan(1, 1, 1, 16384, 128, fab.ATTN_BF16, 0) == b"bwd_fused_kernel"         # equal units
+    assert plan(2, 16, 16, 1024, 64, fab.ATTN_BF16, 1) == b"bwd_fused_kernel"         # 3 units per compute unit
+    assert plan(1, 16, 16, 1024, 128, fab.ATTN_BF16, 1) == b"bwd_fused_kernel"        # too little to gain
     assert plan(1, 8, 8, 16384, 128, fab.ATTN_BF16, 1) == b"bwd_dkdv_kernel+bwd_dq_kernel"
     assert plan(1, 32, 8, 1024, 128, fab.ATTN_BF16, 1) == b"bwd_dkdv_kernel+dkdv_split_sum_kernel+bwd_dq_kernel"
     assert plan(4, 16, 16, 4096, 64, fab.ATTN_BF16, 1, with_dq=0) == b"bwd_dkdv_kernel+bwd_dq_kernel"

@@ -103,12 +103,14 @@ def test_long_sequence_all_heads_bench_step():
         assert e <= TOL[w.dtype], n
 
 
-def test_one_head_share_full_oracle():
+@pytest.mark.parametrize("with_dq", [False, True], ids=["four_calls", "bench_step"])
+def test_one_head_share_full_oracle(with_dq):
     """One head at N = 16384 (256 work units: the combined dK/dV + dQ launch at
-    full length), every output against the oracle."""
+    full length; given dQ, its 32 heaviest key blocks split by query range),
+    every output against the oracle."""
     w = workloads.WORKLOADS["bf16_causal_b1h1_n16384_d128"]
     x = workloads.make_inputs(w)
-    got = run_gpu(w, x)
+    got = run_gpu(w, x, with_dq=with_dq)
     print(f"[{w.name}] kernels done; oracle", flush=True)
     ref = oracle_kv_heads(w, x, 0, [0])
     for n in ("O", "LSE", "D", "dQ", "dK", "dV"):
