@@ -18,6 +18,7 @@ SEQUENCES = [
     [(2, 8, 8, 1024, 64, "bf16", True, False), (1, 2, 2, 200, 64, "bf16", False, False)],      # combined launch
     [(1, 4, 2, 300, 128, "fp32", True, True), (1, 2, 1, 130, 64, "fp32", False, True)],       # fp32, fixed order
     [(1, 2, 2, 257, 64, "fp32", True, False), (1, 1, 1, 100, 64, "fp32", True, False)],       # fp32 atomics
+    [(1, 2, 1, 3000, 128, "bf16", True, False), (1, 2, 2, 4096, 64, "bf16", True, False)],    # split units
 ]
 
 
@@ -41,7 +42,8 @@ def _reference(w, q, k, v, do, o, lse, det):
     return dq, dk, dv
 
 
-@pytest.mark.parametrize("seq", SEQUENCES, ids=["bf16_split", "bf16_combined", "fp32_det", "fp32_atomic"])
+@pytest.mark.parametrize("seq", SEQUENCES, ids=["bf16_split", "bf16_combined", "fp32_det", "fp32_atomic",
+                                                 "bf16_split_units"])
 def test_noalloc_matches_attn_bwd_with_dq(seq):
     for n, case in enumerate(seq):
         det = case[7]
