@@ -14,7 +14,6 @@
 #include "bwd_dq_block.h"
 
 #include <algorithm>
-#include <vector>
 
 namespace fabwd {
 
@@ -205,15 +204,19 @@ FusedSplit fused_split(const Problem& p, bool with_dq) {
   const int n_kb = (p.N + dkdv::BC - 1) / dkdv::BC, n_qb = (p.N + dq::BQ - 1) / dq::BQ;
   const int64_t BHkv = int64_t(p.B) * p.H_kv, BHq = int64_t(p.B) * p.H;
   // Unit weights in dispatch order (key blocks from the first, query blocks
-  // from the last) and their suffix maxima.
-  std::vector<int64_t> kv(n_kb), q(n_qb), kv_suf(n_kb + 1, 0), q_suf(n_qb + 1, 0);
+  // from the last) and their suffix maxima, in fixed arrays (no allocation:
+  // the combined launch has at most kFusedMaxBlocks units of each kind, so
+  // at most that many blocks per head).
+  int kv[kFusedMaxBlocks], q[kFusedMaxBlocks], kv_suf[kFusedMaxBlocks + 1], q_suf[kFusedMaxBlocks + 1];
+  if (n_kb > kFusedMaxBlocks || n_qb > kFusedMaxBlocks) return r;
+  kv_suf[n_kb] = q_suf[n_qb] = 0;
   int64_t total = 0;
-  for (int j = 0; j < n_kb; ++j) total += BHkv * (kv[j] = int64_t(G) * kblock_tiles(p, j));
+  for (int j = 0; j < n_kb; ++j) total += BHkv * (kv[j] = G * kblock_tiles(p, j));
   for (int i = 0; i < n_qb; ++i) total += BHq * (q[i] = qblock_steps(p, n_qb - 1 - i));
   for (int j = n_kb - 1; j >= 0; --j) kv_suf[j] = std::max(kv_suf[j + 1], kv[j]);
   for (int i = n_qb - 1; i >= 0; --i) q_suf[i] = std::max(q_suf[i + 1], q[i]);
   const int64_t avg = (total + kComputeUnits - 1) / kComputeUnits;
-  const int64_t before = std::max({kv_suf[0], q_suf[0], avg});
+  const int64_t before = std::max<int64_t>({kv_suf[0], q_suf[0], avg});
   if (std::max(kv_suf[0], q_suf[0]) <= avg) return r;
   // Room: B*H*N*d floats; a split key block takes 4 BC x d tiles per kv head,
   // a split query block 2 BQ x d tiles per query head.
@@ -221,12 +224,11 @@ FusedSplit fused_split(const Problem& p, bool with_dq) {
   const int64_t kv_tile = 4 * BHkv * dkdv::BC * p.d, q_tile = 2 * BHq * dq::BQ * p.d;
   // best_q[c]: the least heaviest-dQ weight with at most c query blocks split
   // (each split block must keep a step in both halves), and its count.
-  std::vector<int64_t> best_q(n_qb + 1);
-  std::vector<int> best_qn(n_qb + 1);
-  int64_t q_half = 0;
+  int best_q[kFusedMaxBlocks + 1], best_qn[kFusedMaxBlocks + 1];
+  int q_half = 0;
   bool q_ok = true;
   for (int c = 0; c <= n_qb; ++c) {
-    const int64_t w = std::max(q_half, q_suf[c]);
+    const int w = std::max(q_half, q_suf[c]);
     if (c == 0 || w < best_q[c - 1]) { best_q[c] = w; best_qn[c] = c; }
     else { best_q[c] = best_q[c - 1]; best_qn[c] = best_qn[c - 1]; }
     if (c < n_qb) {
@@ -236,14 +238,14 @@ FusedSplit fused_split(const Problem& p, bool with_dq) {
     }
   }
   int64_t best = before;
-  int64_t kv_half = 0;
+  int kv_half = 0;
   for (int a = 0; a <= n_kb; ++a) {
     if (a * kv_tile > room) break;
     const int c = int(std::min<int64_t>(n_qb, (room - a * kv_tile) / q_tile));
-    const int64_t cost = std::max({kv_half, kv_suf[a], best_q[c], avg}) + ((a + best_qn[c]) > 0 ? kSumCost : 0);
+    const int64_t cost = std::max<int64_t>({kv_half, kv_suf[a], best_q[c], avg}) + ((a + best_qn[c]) > 0 ? kSumCost : 0);
     if (cost < best) { best = cost; r.kv = a; r.q = best_qn[c]; }
     if (a == n_kb || kblock_tiles(p, a) < 2) break;
-    kv_half = std::max(kv_half, int64_t(G) * ((kblock_tiles(p, a) + 1) / 2));
+    kv_half = std::max(kv_half, G * ((kblock_tiles(p, a) + 1) / 2));
   }
   r.floats = r.kv * kv_tile + r.q * q_tile;
   return r;
