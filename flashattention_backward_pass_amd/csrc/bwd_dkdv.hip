@@ -26,30 +26,7 @@ __global__ __launch_bounds__(256) void dkdv_split_sum_kernel(const float* __rest
                                                              bf16_t* __restrict__ dV, float scale) {
   const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 8;
   if (i >= elems) return;
-  float k[8], v[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) k[e] = v[e] = 0.f;
-  for (int sp = 0; sp < n_split; ++sp) {
-    const f32x4_t* pk = reinterpret_cast<const f32x4_t*>(part + sp * elems + i);
-    const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(part + (n_split + sp) * elems + i);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const f32x4_t a = pk[h], c = pv[h];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        k[4 * h + e] += a[e];
-        v[4 * h + e] += c[e];
-      }
-    }
-  }
-  u32x4_t ko, vo;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    ko[e] = pack_bf16x2(k[2 * e] * -scale, k[2 * e + 1] * -scale);
-    vo[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-  }
-  *reinterpret_cast<u32x4_t*>(dK + i) = ko;
-  *reinterpret_cast<u32x4_t*>(dV + i) = vo;
+  dkdv::split_sum8(part, n_split, elems, i, dK, dV, scale);
 }
 
 }  // namespace
@@ -63,7 +40,7 @@ namespace {
 
 template <int D, bool SOFTCAP, bool DROPOUT>
 hipError_t dkdv_t(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                  const float* Dv, void* dK, void* dV, float* scratch, hipStream_t s) {
+                  const float* Dv, void* dK, void* dV, float* scratch, bool sum_later, hipStream_t s) {
   const int BH = p.B * p.H_kv;
   const int n_kblk = (p.N + BC - 1) / BC;
   // Grouped-query heads with few work units: the heaviest (first causal)
@@ -77,7 +54,7 @@ hipError_t dkdv_t(const Problem& p, const void* Q, const void* K, const void* V,
                      static_cast<const bf16_t*>(V), static_cast<const bf16_t*>(dO), LSE, Dv,
                      static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV), p.H, p.H_kv, p.N, BH, p.scale, p.softcap,
                      p.wl, p.wr, n_split, n_split > 1 ? scratch : nullptr, p.drop());
-  if (n_split == 1) return hipGetLastError();
+  if (n_split == 1 || sum_later) return hipGetLastError();
   const int64_t elems = int64_t(BH) * p.N * D;
   const unsigned blocks = unsigned((elems / 8 + 255) / 256);
   hipLaunchKernelGGL(dkdv_split_sum_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(scratch),
@@ -87,21 +64,21 @@ hipError_t dkdv_t(const Problem& p, const void* Q, const void* K, const void* V,
 
 template <int D>
 hipError_t dkdv_d(const Problem& p, const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                  const float* Dv, void* dK, void* dV, float* scratch, hipStream_t s) {
+                  const float* Dv, void* dK, void* dV, float* scratch, bool sum_later, hipStream_t s) {
   if (p.dropout)
-    return p.softcap > 0.f ? dkdv_t<D, true, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s)
-                           : dkdv_t<D, false, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s);
-  return p.softcap > 0.f ? dkdv_t<D, true, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s)
-                         : dkdv_t<D, false, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s);
+    return p.softcap > 0.f ? dkdv_t<D, true, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, sum_later, s)
+                           : dkdv_t<D, false, true>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, sum_later, s);
+  return p.softcap > 0.f ? dkdv_t<D, true, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, sum_later, s)
+                         : dkdv_t<D, false, false>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, sum_later, s);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_dkdv_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                                 const float* LSE, const float* Dv, void* dK, void* dV, float* scratch,
-                                hipStream_t s) {
-  return p.d == 64 ? dkdv_d<64>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s)
-                   : dkdv_d<128>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, s);
+                                bool sum_later, hipStream_t s) {
+  return p.d == 64 ? dkdv_d<64>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, sum_later, s)
+                   : dkdv_d<128>(p, Q, K, V, dO, LSE, Dv, dK, dV, scratch, sum_later, s);
 }
 
 }  // namespace fabwd

@@ -70,6 +70,38 @@ struct Cursor {
   int bh;        // b*H + h, the query head (dropout generator counter)
 };
 
+// Eight elements (from element i, a multiple of 8) of the head-split sum:
+// dK = -tau * sum_sp partial_k[sp], dV = sum_sp partial_v[sp], added in split
+// order and rounded to bf16.  The partials are [2][n_split][elems] floats
+// (dK planes, then dV planes), elems = B*H_kv*N*D.
+__device__ __forceinline__ void split_sum8(const float* __restrict__ part, int n_split, int64_t elems, int64_t i,
+                                           bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, float scale) {
+  float k[8], v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) k[e] = v[e] = 0.f;
+  for (int sp = 0; sp < n_split; ++sp) {
+    const f32x4_t* pk = reinterpret_cast<const f32x4_t*>(part + sp * elems + i);
+    const f32x4_t* pv = reinterpret_cast<const f32x4_t*>(part + (n_split + sp) * elems + i);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4_t a = pk[h], c = pv[h];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k[4 * h + e] += a[e];
+        v[4 * h + e] += c[e];
+      }
+    }
+  }
+  u32x4_t ko, vo;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ko[e] = pack_bf16x2(k[2 * e] * -scale, k[2 * e + 1] * -scale);
+    vo[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+  }
+  *reinterpret_cast<u32x4_t*>(dK + i) = ko;
+  *reinterpret_cast<u32x4_t*>(dV + i) = vo;
+}
+
 // Key k is visible to query q iff q - wl <= k <= q + wr and k < N (causal:
 // wr = 0; an unbounded side is N).
 template <int D, bool SOFTCAP, bool DROPOUT>

@@ -15,8 +15,9 @@ const char* bwd_kernels(const Problem& p, bool with_dq) {
   if (p.dtype == 1) {
     if (bwd_fused_fits(p))
       return fused_split(p, with_dq).floats > 0 ? "bwd_fused_kernel+fused_partial_sum_kernel" : "bwd_fused_kernel";
-    return dkdv_split_count(p, true) > 1 ? "bwd_dkdv_kernel+dkdv_split_sum_kernel+bwd_dq_kernel"
-                                         : "bwd_dkdv_kernel+bwd_dq_kernel";
+    // Given dQ, the dQ kernel also adds the head-split partials.
+    return dkdv_split_count(p, true) > 1 && !with_dq ? "bwd_dkdv_kernel+dkdv_split_sum_kernel+bwd_dq_kernel"
+                                                     : "bwd_dkdv_kernel+bwd_dq_kernel";
   }
   if (p.deterministic)
     return with_dq ? "bwd_simple_kernel+bwd_dq_simple_kernel+dq_convert_kernel"
@@ -36,9 +37,13 @@ hipError_t launch_bwd(const Problem& p, const void* Q, const void* K, const void
     if (bwd_fused_fits(p)) return launch_bwd_fused_mfma(p, Q, K, V, dO, LSE, D, dK, dV, dQacc, dQ, s);
     // dQaccum is overwritten by the dQ kernel afterwards (or no longer
     // needed): until then the dK/dV kernel may keep partial sums in it.
-    hipError_t e = launch_bwd_dkdv_mfma(p, Q, K, V, dO, LSE, D, dK, dV, dQacc, s);
+    // Given dQ, the dQ kernel leaves dQaccum alone, so it can also add the
+    // head-split partials (no separate sum launch).
+    const bool sum_in_dq = dQ != nullptr && dkdv_split_count(p, true) > 1;
+    hipError_t e = launch_bwd_dkdv_mfma(p, Q, K, V, dO, LSE, D, dK, dV, dQacc, sum_in_dq, s);
     if (e != hipSuccess) return e;
-    return launch_bwd_dq_mfma(p, Q, K, V, dO, LSE, D, dQacc, dQ, s);
+    return launch_bwd_dq_mfma(p, Q, K, V, dO, LSE, D, dQacc, dQ, sum_in_dq ? dK : nullptr,
+                              sum_in_dq ? dV : nullptr, s);
   }
   // fp32: dQ partials added with atomics (the pages' scheme), or, in
   // deterministic mode, dK/dV alone plus a query-block-outer dQ kernel.

@@ -69,12 +69,17 @@ hipError_t launch_bwd_dq_simple(const Problem& p, const void* Q, const void* K, 
 // (query blocks outer); the dQ kernel overwrites dQaccum, or, given dQout,
 // writes dQ = scale * acc in bf16 instead and leaves dQaccum alone.
 // scratch: B*H*N*d floats the kernel may use for partial sums before the
-// dQ kernel overwrites them (dQaccum), or nullptr.
+// dQ kernel overwrites them (dQaccum), or nullptr.  With sum_later the
+// head-split partials are left for the dQ kernel to add (given dQout, pass
+// dK and dV to launch_bwd_dq_mfma then).
 hipError_t launch_bwd_dkdv_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
                                 const float* LSE, const float* Dv, void* dK, void* dV, float* scratch,
-                                hipStream_t s);
+                                bool sum_later, hipStream_t s);
+// dK, dV: non-null (with dQout) when the dK/dV launch left head-split
+// partials in dQacc for this kernel to add; else nullptr.
 hipError_t launch_bwd_dq_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,
-                              const float* LSE, const float* D, float* dQacc, void* dQout, hipStream_t s);
+                              const float* LSE, const float* D, float* dQacc, void* dQout, void* dK, void* dV,
+                              hipStream_t s);
 // Workgroups sharing each (b, kv head, key block) unit of the dK/dV kernel:
 // 2 for grouped heads (G >= 4) with few units, whose fp32 partials then use
 // the scratch space (dQaccum) before the dQ kernel overwrites it; else 1.

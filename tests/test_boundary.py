@@ -278,7 +278,11 @@ def test_bwd_kernels_query(lib):
     assert plan(2, 16, 16, 1024, 64, fab.ATTN_BF16, 1) == b"bwd_fused_kernel"         # 3 units per compute unit
     assert plan(1, 16, 16, 1024, 128, fab.ATTN_BF16, 1) == b"bwd_fused_kernel"        # too little to gain
     assert plan(1, 8, 8, 16384, 128, fab.ATTN_BF16, 1) == b"bwd_dkdv_kernel+bwd_dq_kernel"
-    assert plan(1, 32, 8, 1024, 128, fab.ATTN_BF16, 1) == b"bwd_dkdv_kernel+dkdv_split_sum_kernel+bwd_dq_kernel"
+    # Grouped heads with few units: the dK/dV work is split over two workgroups
+    # per unit; given dQ the dQ kernel adds the partials, else a sum launch.
+    assert plan(1, 32, 8, 1024, 128, fab.ATTN_BF16, 1) == b"bwd_dkdv_kernel+bwd_dq_kernel"
+    assert plan(1, 32, 8, 1024, 128, fab.ATTN_BF16, 1, with_dq=0) == \
+        b"bwd_dkdv_kernel+dkdv_split_sum_kernel+bwd_dq_kernel"
     assert plan(4, 16, 16, 4096, 64, fab.ATTN_BF16, 1, with_dq=0) == b"bwd_dkdv_kernel+bwd_dq_kernel"
 
 
