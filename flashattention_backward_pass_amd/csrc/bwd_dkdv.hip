@@ -10,7 +10,8 @@ using dkdv::BC;
 using dkdv::kThreads;
 
 template <int D, bool SOFTCAP, bool DROPOUT>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    dkdv::kWavesPerSimd<D, SOFTCAP, DROPOUT>, dkdv::kWavesPerSimd<D, SOFTCAP, DROPOUT>))) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int H, int H_kv, int N, int BH, float scale,

@@ -63,6 +63,14 @@ constexpr int kThreads = 256;
 constexpr int BC = 128;  // keys per workgroup
 constexpr int BR = 64;   // query rows per inner iteration
 
+// Waves per SIMD of the kernels that run this work unit.  d = 128 needs the
+// whole register file of a SIMD lane (one wave); at d = 64 two workgroups
+// share a CU, each wave within 256 registers (all VGPRs: the K, V slices are
+// not pinned to AGPRs there), except with both soft cap and dropout, which
+// would spill.
+template <int D, bool SOFTCAP, bool DROPOUT>
+constexpr int kWavesPerSimd = (D == 64 && !(SOFTCAP && DROPOUT)) ? 2 : 1;
+
 // Position in the sequence of query tiles of a workgroup.
 struct Cursor {
   int q0;        // first row of the query block
@@ -173,9 +181,11 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
       kreg[c] = load_bf16x8(K + row + 16 * c + 8 * g);
       const u32x4_t vb = *reinterpret_cast<const u32x4_t*>(V + row + 16 * c + 8 * g);
       vreg[c] = __builtin_bit_cast(bf16x8_t, vb ^ 0x80008000u);
-      // Only matrix instructions read them: keep them in AGPRs.
-      asm volatile("" : "+a"(kreg[c]));
-      asm volatile("" : "+a"(vreg[c]));
+      // Only matrix instructions read them: keep them in AGPRs (d = 128).
+      if (D == 128) {
+        asm volatile("" : "+a"(kreg[c]));
+        asm volatile("" : "+a"(vreg[c]));
+      }
     }
   }
 

@@ -35,7 +35,8 @@ constexpr int64_t kFusedMaxBlocks = 1024;
 // kind are numbered split halves first ((block i, half h, head x) at
 // 2 BH i + BH h + x), then the unsplit blocks.
 template <int D, bool SOFTCAP, bool DROPOUT>
-__global__ __launch_bounds__(kThreads, 1) void bwd_fused_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    dkdv::kWavesPerSimd<D, SOFTCAP, DROPOUT>, dkdv::kWavesPerSimd<D, SOFTCAP, DROPOUT>))) void bwd_fused_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, float* __restrict__ dQacc, bf16_t* __restrict__ dQout, int H,
