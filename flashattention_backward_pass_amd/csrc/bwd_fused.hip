@@ -21,10 +21,13 @@ namespace {
 
 static_assert(dkdv::kThreads == dq::kThreads, "one workgroup size for both kinds of unit");
 constexpr int kThreads = dkdv::kThreads;
-// Grids of at most this many workgroups (four per compute unit) take the
-// combined launch: measured faster up to 1024 (6-19 % at 1024 workgroups),
-// slower at 2048 (5-10 %, where the dQ units lose their second wave per SIMD).
-constexpr int64_t kFusedMaxBlocks = 1024;
+// Grids of at most this many workgroups take the combined launch.  d = 128
+// (one workgroup per CU): measured faster up to 1024 (6-19 % at 1024
+// workgroups), slower at 2048 (5-10 %, where the dQ units lose their second
+// wave per SIMD).  d = 64 (two workgroups per CU, like the dQ kernel):
+// faster up to 2048 (0.3-5.5 %).
+constexpr int64_t kFusedMaxBlocks = 2048;
+constexpr int64_t fused_max_blocks(int d) { return d == 64 ? kFusedMaxBlocks : kFusedMaxBlocks / 2; }
 
 // With dQ given, dQaccum is free for partial sums: the heaviest units of a
 // causal (or windowed) problem, the first `qblocks` key blocks of every kv
@@ -254,7 +257,7 @@ FusedSplit fused_split(const Problem& p, bool with_dq) {
 
 bool bwd_fused_fits(const Problem& p) {
   return p.dtype == 1 && dkdv_split_count(p, true) == 1 &&
-         int64_t(dkdv_units(p)) + int64_t(dq_units(p)) <= kFusedMaxBlocks;
+         int64_t(dkdv_units(p)) + int64_t(dq_units(p)) <= fused_max_blocks(p.d);
 }
 
 hipError_t launch_bwd_fused_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,

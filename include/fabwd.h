@@ -141,7 +141,8 @@ int attn_bwd_preprocess(const attn_params* p, const void* O, const void* dO,
  *         shares each group's heads over two workgroups and keeps their fp32
  *         partial sums in dQaccum until a fixed-order sum writes dK, dV; the
  *         dQ kernel then overwrites dQaccum.  Problems with few work units
- *         (no head split, at most 1024 workgroups for both kernels) run both
+ *         (no head split, at most 1024 workgroups for both kernels at
+ *         d = 128, 2048 at d = 64) run both
  *         kinds of work unit in one launch; the results are the same bits.
  *   fp32, deterministic = 0: one kernel adds the dQ partials of each key
  *         block into the zeroed dQaccum with fp32 atomics ([CB] 6.2); the

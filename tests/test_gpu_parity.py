@@ -119,13 +119,17 @@ def test_one_head_share_full_oracle(with_dq):
         assert e <= TOL[w.dtype], n
 
 
+@pytest.mark.parametrize("H,plan", [(8, "bwd_fused_kernel"), (16, "bwd_dkdv_kernel+bwd_dq_kernel")],
+                         ids=["combined_2048", "standalone_4096"])
 @pytest.mark.parametrize("cap,drop", [(0.0, None), (10.0, (0.1, 77, 2))], ids=["plain", "softcap_dropout"])
-def test_standalone_kernels_d64(cap, drop):
-    """B=8 H=8 N=2048 d=64 causal: 1024 dK/dV and 1024 dQ work units, more than
-    the combined launch takes, so the two kernels run one after the other.
-    Full oracle on the first and last heads."""
-    w = workloads.custom(8, 8, 8, 2048, 64, "bf16", True, cap, seed=64, name="standalone_d64", dropout=drop)
+def test_many_units_d64(cap, drop, H, plan):
+    """B=8 N=2048 d=64 causal at two workgroups per CU: H=8 gives 1024 dK/dV and
+    1024 dQ work units, the largest grid the combined launch takes at d = 64;
+    H=16 twice that, so the two kernels run one after the other.  Full oracle
+    on the first and last heads."""
+    w = workloads.custom(8, H, H, 2048, 64, "bf16", True, cap, seed=64, name=f"many_units_d64_h{H}", dropout=drop)
     x = workloads.make_inputs(w)
+    assert fab.attn_bwd_kernels(x["Q"], x["K"], causal=True, softcap=cap, dropout=drop, with_dq=False) == plan
     got = run_gpu(w, x)
     for b, g in ((0, 0), (w.B - 1, w.H_kv - 1)):
         ref = oracle_kv_heads(w, x, b, [g])
