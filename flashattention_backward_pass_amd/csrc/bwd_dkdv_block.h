@@ -119,7 +119,7 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
                                            bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int H, int H_kv, int N,
                                            int BH, float scale, float softcap, int wl, int wr, int n_split,
                                            float* __restrict__ part, Dropout drop, unsigned block,
-                                           int qhalf = -1, int qblocks = 0) {
+                                           int qhalf = -1, int qblocks = 0, unsigned* counters = nullptr) {
   constexpr int KC = D / 16;  // 16-wide k chunks over d
   constexpr int NT = D / 32;  // 32-wide column tiles over d
   // Double buffers as separate variables: the compiler gives each LDS
@@ -152,8 +152,9 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
   // qhalf >= 0 (combined launch, n_split == 1) the caller has
   // decoded the unit: `block` is bh + BH * jblk and this workgroup takes half
   // qhalf of the key block's query tiles (0: the later ones, 1: the earlier
-  // ones), writing fp32 partials for fused_partial_sum_kernel: tile
-  // (2 qhalf + tensor) * BH * qblocks + bh * qblocks + jblk of BC x D floats.
+  // ones); the two halves hand the tile over through slot bh * qblocks + jblk
+  // of `part` (dK then dV, BC x D floats each) and the counter of the same
+  // index (split_arrive_first).
   const int unit = block % (BH * n_split);
   const int bh = unit % BH, split = unit / BH;
   const int jblk = block / (BH * n_split);
@@ -567,26 +568,42 @@ __device__ __forceinline__ void dkdv_block(const bf16_t* __restrict__ Q, const b
     float* t1 = reinterpret_cast<float*>(sQO1);
     float* tw = w < 2 ? t0 : t1;
     const int row0 = kw - (w < 2 ? 0 : BC / 2);
+    // Head split: the raw partials go to their planes.  Query-range split:
+    // the first half to finish writes its partials to the unit's slot, the
+    // second adds them to its own and writes dK, dV.
+    __shared__ unsigned s_arrival;
+    const int64_t slot = int64_t(bh) * qblocks + jblk;
+    const bool to_part = qhalf < 0 || split_arrive_first(counters + slot, &s_arrival, tid);
     float* dst_k;
     float* dst_v;
     if (qhalf >= 0) {
-      const int64_t tiles = int64_t(BH) * qblocks;
-      const int64_t t = int64_t(bh) * qblocks + jblk;
-      dst_k = part + ((2 * qhalf) * tiles + t) * (BC * D);
-      dst_v = part + ((2 * qhalf + 1) * tiles + t) * (BC * D);
+      dst_k = part + slot * (2 * BC * D);
+      dst_v = dst_k + BC * D;
+      if (!to_part) split_wait(counters + slot, tid);
     } else {
       dst_k = part + split * plane + (kv_off + k0) * D;
       dst_v = part + (n_split + split) * plane + (kv_off + k0) * D;
     }
-    stage_acc<float, NT, D>(tw, row0, dk_acc, 1.f, lane);
-    __syncthreads();
-    stage_copy_rows<float, D, kThreads>(dst_k, t0, BC / 2, valid, tid);
-    stage_copy_rows<float, D, kThreads>(dst_k + (BC / 2) * D, t1, BC / 2, valid - BC / 2, tid);
-    __syncthreads();
-    stage_acc<float, NT, D>(tw, row0, dv_acc, v_scale, lane);
-    __syncthreads();
-    stage_copy_rows<float, D, kThreads>(dst_v, t0, BC / 2, valid, tid);
-    stage_copy_rows<float, D, kThreads>(dst_v + (BC / 2) * D, t1, BC / 2, valid - BC / 2, tid);
+#pragma unroll
+    for (int tensor = 0; tensor < 2; ++tensor) {
+      stage_acc<float, NT, D>(tw, row0, tensor == 0 ? dk_acc : dv_acc, tensor == 0 ? 1.f : v_scale, lane);
+      __syncthreads();
+      float* dst = tensor == 0 ? dst_k : dst_v;
+      if (to_part && qhalf < 0) {
+        stage_copy_rows<float, D, kThreads>(dst, t0, BC / 2, valid, tid);
+        stage_copy_rows<float, D, kThreads>(dst + (BC / 2) * D, t1, BC / 2, valid - BC / 2, tid);
+      } else if (to_part) {
+        stage_store_rows_coherent<D, kThreads>(dst, t0, BC / 2, valid, tid);
+        stage_store_rows_coherent<D, kThreads>(dst + (BC / 2) * D, t1, BC / 2, valid - BC / 2, tid);
+      } else {
+        bf16_t* out = (tensor == 0 ? dK : dV) + (kv_off + k0) * D;
+        const float mul = tensor == 0 ? -scale : 1.f;
+        stage_add_rows<D, kThreads>(out, t0, dst, BC / 2, valid, mul, tid);
+        stage_add_rows<D, kThreads>(out + (BC / 2) * D, t1, dst + (BC / 2) * D, BC / 2, valid - BC / 2, mul, tid);
+      }
+      __syncthreads();
+    }
+    if (qhalf >= 0 && to_part) split_publish(counters + slot, tid);
   }
 }
 

@@ -50,7 +50,7 @@ __device__ __forceinline__ void dq_block(
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     float* __restrict__ dQacc, bf16_t* __restrict__ dQout, int H, int H_kv, int N, int BHq, float scale,
     float softcap, int wl, int wr, Dropout drop, unsigned block, int khalf = -1, int qq = 0,
-    float* __restrict__ part = nullptr) {
+    float* __restrict__ part = nullptr, unsigned* counters = nullptr) {
   constexpr int KC = D / 16;
   constexpr int NT = D / 32;
   // Double buffers as separate variables: the compiler gives each LDS
@@ -148,9 +148,9 @@ __device__ __forceinline__ void dq_block(
 
   // Key blocks [s_lo, s_hi) hold every key that some row of this block sees.
   // With khalf >= 0 (combined launch) this workgroup takes half khalf of them
-  // (0: the later ones, 1: the earlier ones) and writes its unscaled fp32 sum
-  // as a partial tile, khalf * BHq * qq + bhq * qq + (n_qblk - 1 - iblk) of
-  // BQ x D floats in `part`, for the sum kernel that follows the launch.
+  // (0: the later ones, 1: the earlier ones); the two halves hand the tile
+  // over through slot bhq * qq + (n_qblk - 1 - iblk) of `part` (BQ x D
+  // floats) and the counter of the same index (split_arrive_first).
   const int q_hi = min(q0 + BQ, N) - 1;  // last valid row
   int s_lo = max(0, q0 - wl) / BK;
   int s_hi = (min(N, q_hi + wr + 1) + BK - 1) / BK;
@@ -319,12 +319,27 @@ __device__ __forceinline__ void dq_block(
     // BQ x D fp32 = both buffers: rows 0-63 in buffer 0, rows 64-127 in buffer 1.
     float* t0 = reinterpret_cast<float*>(sKV0);
     float* t1 = reinterpret_cast<float*>(sKV1);
-    float* dst = dQacc + (q_off + q0) * D;
-    if (khalf >= 0) dst = part + ((int64_t(khalf) * BHq + bhq) * qq + (n_qblk - 1 - iblk)) * (BQ * D);
+    // Key-range split: the first half to finish writes its fp32 sum to the
+    // unit's slot, the second adds it to its own and writes dQ.
+    __shared__ unsigned s_arrival;
+    const int64_t slot = int64_t(bhq) * qq + (n_qblk - 1 - iblk);
+    const bool to_part = khalf < 0 || split_arrive_first(counters + slot, &s_arrival, tid);
+    float* dst = khalf >= 0 ? part + slot * (BQ * D) : dQacc + (q_off + q0) * D;
     stage_acc<float, NT, D>(w < 2 ? t0 : t1, 32 * w - (w < 2 ? 0 : BQ / 2), dq_acc, 1.f, lane);
+    if (!to_part) split_wait(counters + slot, tid);
     __syncthreads();
-    stage_copy_rows<float, D, kThreads>(dst, t0, BQ / 2, valid, tid);
-    stage_copy_rows<float, D, kThreads>(dst + (BQ / 2) * D, t1, BQ / 2, valid - BQ / 2, tid);
+    if (to_part && khalf < 0) {
+      stage_copy_rows<float, D, kThreads>(dst, t0, BQ / 2, valid, tid);
+      stage_copy_rows<float, D, kThreads>(dst + (BQ / 2) * D, t1, BQ / 2, valid - BQ / 2, tid);
+    } else if (to_part) {
+      stage_store_rows_coherent<D, kThreads>(dst, t0, BQ / 2, valid, tid);
+      stage_store_rows_coherent<D, kThreads>(dst + (BQ / 2) * D, t1, BQ / 2, valid - BQ / 2, tid);
+      split_publish(counters + slot, tid);
+    } else {
+      bf16_t* out = dQout + (q_off + q0) * D;
+      stage_add_rows<D, kThreads>(out, t0, dst, BQ / 2, valid, scale, tid);
+      stage_add_rows<D, kThreads>(out + (BQ / 2) * D, t1, dst + (BQ / 2) * D, BQ / 2, valid - BQ / 2, scale, tid);
+    }
   }
 }
 

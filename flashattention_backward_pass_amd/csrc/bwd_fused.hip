@@ -14,6 +14,7 @@
 #include "bwd_dq_block.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace fabwd {
 
@@ -32,11 +33,13 @@ constexpr int64_t fused_max_blocks(int d) { return d == 64 ? kFusedMaxBlocks : k
 // With dQ given, dQaccum is free for partial sums: the heaviest units of a
 // causal (or windowed) problem, the first `qblocks` key blocks of every kv
 // head and the last `qq` query blocks of every query head, are each split in
-// two, dK/dV units by query range and dQ units by key range, whose fp32
-// partial tiles go to dQaccum (dK/dV tiles first, then dQ tiles);
-// fused_partial_sum_kernel adds the halves after the launch.  Units of each
-// kind are numbered split halves first ((block i, half h, head x) at
-// 2 BH i + BH h + x), then the unsplit blocks.
+// two, dK/dV units by query range and dQ units by key range.  The two halves
+// of a unit hand the output tile over through dQaccum: the first to finish
+// writes an fp32 partial, the second adds it and writes the result
+// (split_arrive_first).  dQaccum holds the dK/dV slots (2 BC x D floats each),
+// then the dQ slots (BQ x D), then one counter word per split unit, zeroed
+// by the preprocess.  Units of each kind are numbered split halves first
+// ((block i, half h, head x) at 2 BH i + BH h + x), then the unsplit blocks.
 template <int D, bool SOFTCAP, bool DROPOUT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     dkdv::kWavesPerSimd<D, SOFTCAP, DROPOUT>, dkdv::kWavesPerSimd<D, SOFTCAP, DROPOUT>))) void bwd_fused_kernel(
@@ -69,9 +72,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     } else {
       u = unit - n_half + unsigned(BH_q) * unsigned(qq);
     }
-    float* qpart = dQacc + 4 * int64_t(BH_kv) * qblocks * (dkdv::BC * D);
+    const int64_t kv_floats = 2 * int64_t(BH_kv) * qblocks * (dkdv::BC * D);
+    float* qpart = dQacc + kv_floats;
+    unsigned* qcnt = reinterpret_cast<unsigned*>(qpart + int64_t(BH_q) * qq * (dq::BQ * D)) + BH_kv * qblocks;
     dq::dq_block<D, SOFTCAP, DROPOUT>(Q, K, V, dO, LSE, Dv, dQacc, dQout, H, H_kv, N, BH_q, scale, softcap, wl, wr,
-                                      drop, u, khalf, qq, qpart);
+                                      drop, u, khalf, qq, qpart, qcnt);
   } else {
     const unsigned n_half = 2u * unsigned(BH_kv) * unsigned(qblocks);
     int qhalf = -1;
@@ -83,60 +88,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     } else {
       u = unit - n_half + unsigned(BH_kv) * unsigned(qblocks);
     }
+    const int64_t kv_floats = 2 * int64_t(BH_kv) * qblocks * (dkdv::BC * D);
+    unsigned* kcnt = reinterpret_cast<unsigned*>(dQacc + kv_floats + int64_t(BH_q) * qq * (dq::BQ * D));
     dkdv::dkdv_block<D, SOFTCAP, DROPOUT>(Q, K, V, dO, LSE, Dv, dK, dV, H, H_kv, N, BH_kv, scale, softcap, wl, wr,
-                                          1, qhalf >= 0 ? dQacc : nullptr, drop, u, qhalf, qblocks);
+                                          1, qhalf >= 0 ? dQacc : nullptr, drop, u, qhalf, qblocks, kcnt);
   }
-}
-
-// Sums the partial tiles of the split units (fixed order; layout as
-// bwd_fused_kernel writes them): elements [0, BH_kv qblocks BC D) are dK/dV
-// tiles, dK = -tau (p0 + p1) and dV = p0 + p1; the rest are dQ tiles,
-// dQ = tau (p0 + p1), the product and rounding of the convert kernel.
-// 8 elements per thread; rows past N skipped.
-template <int D>
-__global__ __launch_bounds__(256) void fused_partial_sum_kernel(const float* __restrict__ part, int BH_kv,
-                                                                int qblocks, int BH_q, int qq, int N,
-                                                                bf16_t* __restrict__ dK, bf16_t* __restrict__ dV,
-                                                                bf16_t* __restrict__ dQ, float scale) {
-  constexpr int BC = dkdv::BC, BQ = dq::BQ;
-  const int64_t kv_tiles = int64_t(BH_kv) * qblocks, q_tiles = int64_t(BH_q) * qq;
-  const int64_t kv_elems = kv_tiles * BC * D;
-  int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 8;
-  u32x4_t o0, o1;
-  if (i < kv_elems) {
-    const int64_t t = i / (BC * D);
-    const int within = int(i % (BC * D));
-    const int bh = int(t / qblocks), j = int(t % qblocks);
-    const int key = j * BC + within / D;
-    if (key >= N) return;
-    const int64_t out = (int64_t(bh) * N + key) * D + within % D;
-    const float* pk0 = part + i;
-    const float* pv0 = pk0 + kv_elems;
-    const float* pk1 = pv0 + kv_elems;
-    const float* pv1 = pk1 + kv_elems;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o0[e] = pack_bf16x2(-scale * (pk0[2 * e] + pk1[2 * e]), -scale * (pk0[2 * e + 1] + pk1[2 * e + 1]));
-      o1[e] = pack_bf16x2(pv0[2 * e] + pv1[2 * e], pv0[2 * e + 1] + pv1[2 * e + 1]);
-    }
-    *reinterpret_cast<u32x4_t*>(dK + out) = o0;
-    *reinterpret_cast<u32x4_t*>(dV + out) = o1;
-    return;
-  }
-  i -= kv_elems;
-  if (i >= q_tiles * BQ * D) return;
-  const int64_t t = i / (BQ * D);
-  const int within = int(i % (BQ * D));
-  const int bh = int(t / qq), iq = int(t % qq);
-  const int row = ((N + BQ - 1) / BQ - 1 - iq) * BQ + within / D;
-  if (row >= N) return;
-  const int64_t out = (int64_t(bh) * N + row) * D + within % D;
-  const float* p0 = part + 4 * kv_elems + i;
-  const float* p1 = p0 + q_tiles * BQ * D;
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    o0[e] = pack_bf16x2(scale * (p0[2 * e] + p1[2 * e]), scale * (p0[2 * e + 1] + p1[2 * e + 1]));
-  *reinterpret_cast<u32x4_t*>(dQ + out) = o0;
 }
 
 unsigned dkdv_units(const Problem& p) {
@@ -170,11 +126,6 @@ hipError_t fused_t(const Problem& p, const void* Q, const void* K, const void* V
                      static_cast<const bf16_t*>(dO), LSE, Dv, static_cast<bf16_t*>(dK), static_cast<bf16_t*>(dV),
                      dQacc, static_cast<bf16_t*>(dQout), p.H, p.H_kv, p.N, BH, BHq, p.scale, p.softcap, p.wl,
                      p.wr, p.drop(), n1, n2, sp.kv, sp.q);
-  if (sp.kv + sp.q == 0) return hipGetLastError();
-  const int64_t elems = (int64_t(BH) * sp.kv * dkdv::BC + int64_t(BHq) * sp.q * dq::BQ) * D;
-  hipLaunchKernelGGL(fused_partial_sum_kernel<D>, dim3(unsigned((elems / 8 + 255) / 256)), dim3(256), 0, s,
-                     static_cast<const float*>(dQacc), BH, sp.kv, BHq, sp.q, p.N, static_cast<bf16_t*>(dK),
-                     static_cast<bf16_t*>(dV), static_cast<bf16_t*>(dQout), p.scale);
   return hipGetLastError();
 }
 
@@ -196,14 +147,70 @@ hipError_t fused_d(const Problem& p, const void* Q, const void* K, const void* V
 // (both near 1.4 us at d = 128 on one compute unit, measured).  The launch
 // takes about max(heaviest unit, total / compute units); splitting the
 // leading units of a kind (the heaviest under a causal mask) halves them,
-// costs a summing launch of about kSumCost steps and is limited by the
-// room in dQaccum.  The split with the least predicted time is taken when it
-// beats the unsplit launch.
-FusedSplit fused_split(const Problem& p, bool with_dq) {
+// costs a handoff of about kSplitCost steps and is limited by the room in
+// dQaccum.  The split with the least predicted time is taken when it beats
+// the unsplit launch.
+// Makespan, in matrix steps, of the combined launch's units in dispatch
+// order (as bwd_fused_kernel numbers them) when each goes to the workgroup
+// slot that frees first, with key blocks [0, a) and the last c query blocks
+// split in two.  A binary heap of slot finish times in a fixed array.
+int64_t fused_makespan(const Problem& p, int a, int c) {
+  // Workgroup slots: 256 CUs times the workgroups each holds (two at d = 64,
+  // except with soft cap and dropout together).
+  const int slots = p.d == 64 && !(p.softcap > 0.f && p.dropout) ? 512 : 256;
+  const int G = p.H / p.H_kv;
+  const int n_kb = (p.N + dkdv::BC - 1) / dkdv::BC, n_qb = (p.N + dq::BQ - 1) / dq::BQ;
+  const int64_t BHkv = int64_t(p.B) * p.H_kv, BHq = int64_t(p.B) * p.H;
+  const int64_t n1 = BHkv * (n_kb + a), n2 = BHq * (n_qb + c);
+  auto halves = [](int lo, int hi, int h) { const int mid = (lo + hi + 1) / 2; return h == 0 ? hi - mid : mid - lo; };
+  auto kv_weight = [&](int64_t u) -> int64_t {
+    if (u < 2 * BHkv * a) {
+      const int j = int(u / (2 * BHkv)), h = int((u / BHkv) & 1);
+      const int k0 = j * dkdv::BC, k_end = std::min(k0 + dkdv::BC, p.N);
+      return int64_t(G) * halves(std::max(0, k0 - p.wr) / dkdv::BR,
+                                 (std::min(p.N, k_end + p.wl) + dkdv::BR - 1) / dkdv::BR, h);
+    }
+    return int64_t(G) * kblock_tiles(p, int((u - 2 * BHkv * a) / BHkv) + a);
+  };
+  auto q_weight = [&](int64_t u) -> int64_t {
+    if (u < 2 * BHq * c) {
+      const int i = n_qb - 1 - int(u / (2 * BHq)), h = int((u / BHq) & 1);
+      const int q0 = i * dq::BQ, q_hi = std::min(q0 + dq::BQ, p.N) - 1;
+      return halves(std::max(0, q0 - p.wl) / dq::BK, (std::min(p.N, q_hi + p.wr + 1) + dq::BK - 1) / dq::BK, h);
+    }
+    return qblock_steps(p, n_qb - 1 - (int((u - 2 * BHq * c) / BHq) + c));
+  };
+  int64_t heap[512];
+  for (int k = 0; k < slots; ++k) heap[k] = 0;
+  auto place = [&](int64_t w) {  // replace the minimum (root) by root + w, sift down
+    int64_t v = heap[0] + w;
+    int k = 0;
+    for (;;) {
+      int l = 2 * k + 1, m = k;
+      if (l < slots && heap[l] < v) m = l;
+      if (l + 1 < slots && heap[l + 1] < (m == k ? v : heap[m])) m = l + 1;
+      if (m == k) break;
+      heap[k] = heap[m];
+      k = m;
+    }
+    heap[k] = v;
+  };
+  const int64_t m = std::min(n1, n2);
+  for (int64_t u = 0; u < m; ++u) {
+    place(kv_weight(u));
+    place(q_weight(u));
+  }
+  for (int64_t u = m; u < n1; ++u) place(kv_weight(u));
+  for (int64_t u = m; u < n2; ++u) place(q_weight(u));
+  int64_t span = 0;
+  for (int k = 0; k < slots; ++k) span = std::max(span, heap[k]);
+  return span;
+}
+
+FusedSplit fused_split_choice(const Problem& p) {
   FusedSplit r;
-  if (!with_dq || p.dtype != 1 || !bwd_fused_fits(p)) return r;
   constexpr int64_t kComputeUnits = 256;
-  const int64_t kSumCost = p.d == 128 ? 3 : 6;
+  const int64_t kSplitCost = p.d == 128 ? 2 : 4;
   const int G = p.H / p.H_kv;
   const int n_kb = (p.N + dkdv::BC - 1) / dkdv::BC, n_qb = (p.N + dq::BQ - 1) / dq::BQ;
   const int64_t BHkv = int64_t(p.B) * p.H_kv, BHq = int64_t(p.B) * p.H;
@@ -222,10 +229,11 @@ FusedSplit fused_split(const Problem& p, bool with_dq) {
   const int64_t avg = (total + kComputeUnits - 1) / kComputeUnits;
   const int64_t before = std::max<int64_t>({kv_suf[0], q_suf[0], avg});
   if (std::max(kv_suf[0], q_suf[0]) <= avg) return r;
-  // Room: B*H*N*d floats; a split key block takes 4 BC x d tiles per kv head,
-  // a split query block 2 BQ x d tiles per query head.
+  // Room: B*H*N*d floats; a split key block takes a slot of 2 BC x d floats
+  // and a counter word per kv head, a split query block a slot of BQ x d
+  // floats and a counter per query head.
   const int64_t room = BHq * p.N * p.d;
-  const int64_t kv_tile = 4 * BHkv * dkdv::BC * p.d, q_tile = 2 * BHq * dq::BQ * p.d;
+  const int64_t kv_tile = BHkv * (2 * dkdv::BC * p.d + 1), q_tile = BHq * (int64_t(dq::BQ) * p.d + 1);
   // best_q[c]: the least heaviest-dQ weight with at most c query blocks split
   // (each split block must keep a step in both halves), and its count.
   int best_q[kFusedMaxBlocks + 1], best_qn[kFusedMaxBlocks + 1];
@@ -246,13 +254,53 @@ FusedSplit fused_split(const Problem& p, bool with_dq) {
   for (int a = 0; a <= n_kb; ++a) {
     if (a * kv_tile > room) break;
     const int c = int(std::min<int64_t>(n_qb, (room - a * kv_tile) / q_tile));
-    const int64_t cost = std::max<int64_t>({kv_half, kv_suf[a], best_q[c], avg}) + ((a + best_qn[c]) > 0 ? kSumCost : 0);
+    const int64_t cost = std::max<int64_t>({kv_half, kv_suf[a], best_q[c], avg}) + ((a + best_qn[c]) > 0 ? kSplitCost : 0);
     if (cost < best) { best = cost; r.kv = a; r.q = best_qn[c]; }
     if (a == n_kb || kblock_tiles(p, a) < 2) break;
     kv_half = std::max(kv_half, G * ((kblock_tiles(p, a) + 1) / 2));
   }
-  r.floats = r.kv * kv_tile + r.q * q_tile;
+  if (r.kv + r.q == 0) return r;
+  // The bound above misses how whole units pack onto the compute units, and
+  // the chip runs idle units' neighbours faster (it is power-limited), so a
+  // split pays less than the critical path alone says: keep it only if the
+  // list-scheduled makespan drops to kKeepRatio or less (measured: the
+  // splits that paid predicted 0.67-0.69, those that lost 0.75 and 0.90).
+  constexpr int64_t kKeepNum = 72, kKeepDen = 100;
+  if (fused_makespan(p, r.kv, r.q) * kKeepDen > fused_makespan(p, 0, 0) * kKeepNum) return FusedSplit{};
+  r.counter_off = BHkv * r.kv * 2 * dkdv::BC * p.d + BHq * r.q * int64_t(dq::BQ) * p.d;
+  r.counters = int(BHkv * r.kv + BHq * r.q);
+  r.floats = r.counter_off + r.counters;
   return r;
+}
+
+// The choice depends only on the shape and band; a few recent ones are kept
+// (fixed table, no allocation), since every launch and its preprocess ask.
+FusedSplit fused_split(const Problem& p, bool with_dq) {
+  if (!with_dq || p.dtype != 1 || !bwd_fused_fits(p)) return FusedSplit{};
+  struct Entry {
+    int B = -1, H, H_kv, N, d, wl, wr;
+    bool narrow;  // one workgroup per CU at d = 64 (soft cap with dropout)
+    FusedSplit v;
+  };
+  const bool narrow = p.softcap > 0.f && p.dropout;
+  static Entry cache[16];
+  static std::mutex mu;
+  const unsigned slot = (unsigned(p.B) * 131u + unsigned(p.H) * 31u + unsigned(p.H_kv) * 7u + unsigned(p.N) * 3u +
+                         unsigned(p.d) + unsigned(p.wl) * 17u + unsigned(p.wr) * 13u) % 16u;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    const Entry& e = cache[slot];
+    if (e.B == p.B && e.H == p.H && e.H_kv == p.H_kv && e.N == p.N && e.d == p.d && e.wl == p.wl && e.wr == p.wr &&
+        e.narrow == narrow)
+      return e.v;
+  }
+  const FusedSplit v = fused_split_choice(p);
+  std::lock_guard<std::mutex> lock(mu);
+  Entry& e = cache[slot];
+  e.B = p.B; e.H = p.H; e.H_kv = p.H_kv; e.N = p.N; e.d = p.d; e.wl = p.wl; e.wr = p.wr;
+  e.narrow = narrow;
+  e.v = v;
+  return v;
 }
 
 bool bwd_fused_fits(const Problem& p) {

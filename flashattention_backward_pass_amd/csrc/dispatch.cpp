@@ -14,7 +14,7 @@ hipError_t launch_fwd_stats(const Problem& p, const void* Q, const void* K, cons
 const char* bwd_kernels(const Problem& p, bool with_dq) {
   if (p.dtype == 1) {
     if (bwd_fused_fits(p))
-      return fused_split(p, with_dq).floats > 0 ? "bwd_fused_kernel+fused_partial_sum_kernel" : "bwd_fused_kernel";
+      return fused_split(p, with_dq).floats > 0 ? "bwd_fused_kernel:split" : "bwd_fused_kernel";
     // Given dQ, the dQ kernel also adds the head-split partials.
     return dkdv_split_count(p, true) > 1 && !with_dq ? "bwd_dkdv_kernel+dkdv_split_sum_kernel+bwd_dq_kernel"
                                                      : "bwd_dkdv_kernel+bwd_dq_kernel";

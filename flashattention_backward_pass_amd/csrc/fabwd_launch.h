@@ -91,11 +91,15 @@ bool bwd_fused_fits(const Problem& p);
 // Units the combined launch splits in two when dQ is given (its heaviest
 // units under a causal or windowed mask): the first `kv` key blocks of every
 // kv head (dK/dV by query range) and the last `q` query blocks of every query
-// head (dQ by key range); their fp32 partial sums take the first `floats`
-// floats of dQaccum.  All zero when no split is predicted to pay.
+// head (dQ by key range).  Their handoff slots and then `counters` counter
+// words (from float offset counter_off, which the preprocess zeroes) take the
+// first `floats` floats of dQaccum.  All zero when no split is predicted to
+// pay.
 struct FusedSplit {
   int kv = 0, q = 0;
   int64_t floats = 0;
+  int64_t counter_off = 0;
+  int counters = 0;
 };
 FusedSplit fused_split(const Problem& p, bool with_dq);
 hipError_t launch_bwd_fused_mfma(const Problem& p, const void* Q, const void* K, const void* V, const void* dO,

@@ -133,4 +133,93 @@ __device__ __forceinline__ void stage_copy_rows(T* __restrict__ dst, const T* ti
   }
 }
 
+// The handoff of a split work unit's output tile between its two halves.
+// The partial goes through memory with agent-coherent (sc1) 16-byte buffer
+// accesses, the cache policy the memory model gives relaxed agent-scope
+// atomics: no L2 write-back or invalidation is needed (an acquire/release
+// pair would flush and invalidate the whole L2 of both XCDs for every
+// handoff, which measured far slower).  The order is kept by waits: the
+// first half's stores complete (vmcnt 0, then a barrier) before its counter
+// update is issued, and the second half issues its loads only after reading
+// the final count.
+constexpr int kAgentCoherent = 16;  // buffer-access aux bits: sc1
+
+// Rows [0, rows) of a row-major fp32 LDS tile (COLS per row) to dst + row *
+// COLS with agent-coherent 16-byte stores; rows at or past `valid` skipped.
+template <int COLS, int NTHREADS>
+__device__ __forceinline__ void stage_store_rows_coherent(float* dst, const float* tile, int rows, int valid,
+                                                          int tid) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(dst, 0, rows * COLS * 4, 0x00020000);
+  constexpr int kChunks = COLS / 4;
+  for (int i = tid; i < rows * kChunks; i += NTHREADS) {
+    const int row = i / kChunks, c = i % kChunks;
+    if (row < valid) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(tile + row * COLS + 4 * c);
+      __builtin_amdgcn_raw_buffer_store_b128(v, r, (row * COLS + 4 * c) * 4, 0, kAgentCoherent);
+    }
+  }
+}
+
+// Rows [0, rows) of the fp32 LDS tile plus the same rows of `other` (read
+// with agent-coherent loads; row-major, COLS per row), times mul, rounded to
+// bf16 (RNE) and stored to dst + row * COLS with 16-byte stores; rows at or
+// past `valid` are skipped.  The sum is tile + other in fp32, the same value
+// as other + tile.
+template <int COLS, int NTHREADS>
+__device__ __forceinline__ void stage_add_rows(bf16_t* __restrict__ dst, const float* tile, const float* other,
+                                               int rows, int valid, float mul, int tid) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(other), 0, rows * COLS * 4, 0x00020000);
+  constexpr int kChunks = COLS / 8;  // 8 elements: one 16-byte bf16 store
+  for (int i = tid; i < rows * kChunks; i += NTHREADS) {
+    const int row = i / kChunks, c = i % kChunks;
+    if (row < valid) {
+      const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(tile + row * COLS + 8 * c);
+      const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(tile + row * COLS + 8 * c + 4);
+      const f32x4_t b0 = __builtin_bit_cast(
+          f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (row * COLS + 8 * c) * 4, 0, kAgentCoherent));
+      const f32x4_t b1 = __builtin_bit_cast(
+          f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (row * COLS + 8 * c + 4) * 4, 0, kAgentCoherent));
+      u32x4_t o;
+      o[0] = pack_bf16x2(mul * (a0[0] + b0[0]), mul * (a0[1] + b0[1]));
+      o[1] = pack_bf16x2(mul * (a0[2] + b0[2]), mul * (a0[3] + b0[3]));
+      o[2] = pack_bf16x2(mul * (a1[0] + b1[0]), mul * (a1[1] + b1[1]));
+      o[3] = pack_bf16x2(mul * (a1[2] + b1[2]), mul * (a1[3] + b1[3]));
+      *reinterpret_cast<u32x4_t*>(dst + int64_t(row) * COLS + 8 * c) = o;
+    }
+  }
+}
+
+// A counter (zero before the launch) counts the halves' arrivals: the first
+// to arrive writes its fp32 partial (stage_store_rows_coherent), then
+// split_publish raises the counter to 3 once the other has arrived too
+// (2 + 1), or to 2 before (1 + 1, and the other's arrival makes it 3); the
+// second waits in split_wait for 3, adds the partial to its own
+// (stage_add_rows) and writes the result.  Nobody waits for a workgroup that
+// has not yet arrived, so the handoff cannot deadlock whatever the order of
+// dispatch.  The bounded wait is a safety net only (its limit, about a
+// second, is far beyond the partial write it waits for).
+__device__ __forceinline__ bool split_arrive_first(unsigned* counter, unsigned* lds_word, int tid) {
+  if (tid == 0) *lds_word = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return *lds_word == 0u;
+}
+__device__ __forceinline__ void split_publish(unsigned* counter, int tid) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // every thread's partial stores have completed
+  if (tid == 0) __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void split_wait(unsigned* counter, int tid) {
+  if (tid == 0) {
+    for (int it = 0; it < (1 << 22); ++it) {
+      if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 3u) break;
+      __builtin_amdgcn_s_sleep(8);
+    }
+    // Zero again for the next launch (the preprocess zeroes it too).
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 }  // namespace fabwd

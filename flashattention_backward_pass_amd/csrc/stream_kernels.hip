@@ -1,6 +1,8 @@
 // Bandwidth-bound kernels of the backward pass:
 //   bwd_preprocess : D_i = sum_k dO_ik O_ik in fp32, and dQaccum <- 0 for the
-//                    fp32 path (whose backward adds into dQaccum)
+//                    fp32 path (whose backward adds into dQaccum); for bf16,
+//                    the handoff counters of split units in the combined
+//                    launch (a few words of dQaccum) <- 0
 //                    ("解析 FlashAttention（3）：FlashAttention-v1 反向传播", eq (6);
 //                     Inference Cookbook "反向传播算法详解" section 2.1, dPsum
 //                     computed before the backward kernel);
@@ -45,7 +47,9 @@ constexpr int kUnroll = 4;
 template <typename T, int D, bool ZERO_ACC>
 __global__ __launch_bounds__(kThreads) void preprocess_kernel(const T* __restrict__ O, const T* __restrict__ dO,
                                                               float* __restrict__ Dout,
-                                                              float* __restrict__ dQacc, int64_t rows) {
+                                                              float* __restrict__ dQacc, int64_t rows,
+                                                              unsigned* __restrict__ zero_words, int n_zero) {
+  for (int i = blockIdx.x * kThreads + threadIdx.x; i < n_zero; i += gridDim.x * kThreads) zero_words[i] = 0u;
   constexpr int kPerLane = 16 / sizeof(T);      // elements per 16-byte access
   constexpr int L = D / kPerLane;                // lanes per row
   constexpr int kRowsPerGroup = kThreads / L;    // rows covered by the block at once
@@ -137,9 +141,11 @@ hipError_t preprocess_t(const Problem& p, const void* O, const void* dO, float* 
   constexpr int L = D / (16 / sizeof(T));
   const int64_t rows = p.q_rows();
   constexpr bool kZero = sizeof(T) == 4;  // only the fp32 backward accumulates into dQaccum
+  const FusedSplit sp = kZero ? FusedSplit{} : fused_split(p, true);
+  unsigned* zero_words = sp.counters > 0 ? reinterpret_cast<unsigned*>(dQacc + sp.counter_off) : nullptr;
   hipLaunchKernelGGL((preprocess_kernel<T, D, kZero>), dim3(grid_for(rows, kThreads / L * kUnroll)), dim3(kThreads),
                      0, s,
-                     static_cast<const T*>(O), static_cast<const T*>(dO), Dv, dQacc, rows);
+                     static_cast<const T*>(O), static_cast<const T*>(dO), Dv, dQacc, rows, zero_words, sp.counters);
   return hipGetLastError();
 }
 

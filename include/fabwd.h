@@ -112,8 +112,11 @@ int attn_fwd_stats(const attn_params* p, const void* Q, const void* K, const voi
  * attn_bwd_preprocess - D = rowsum(dO o O) ([FA1] eq (6); [CB] 2.1 dPsum),
  * accumulated in float32 in a fixed order (bitwise reproducible).
  * Reads O, dO; writes D [B,H,N].  For fp32 inputs it also zeroes dQaccum
- * [B,H,N,d] (the fp32 backward adds into it); for bf16 inputs dQaccum is not
- * touched (the bf16 backward overwrites it).
+ * [B,H,N,d] (the fp32 backward adds into it); for bf16 inputs it zeroes at
+ * most one word per work unit of dQaccum when attn_bwd_with_dq splits work
+ * units for these parameters (the split units' handoff counters; that call
+ * must get the same dQaccum) and leaves the rest alone (the bf16 backward
+ * overwrites it).
  */
 int attn_bwd_preprocess(const attn_params* p, const void* O, const void* dO,
                         float* D, float* dQaccum, void* stream);
@@ -178,11 +181,13 @@ int attn_bwd_dq_convert(const attn_params* p, const float* dQaccum, void* dQ, vo
  *         unspecified afterwards.  Small causal or windowed problems whose
  *         heaviest work units outweigh the rest take the combined launch
  *         with those units split in two (dK/dV of the first key blocks by
- *         query range, dQ of the last query blocks by key range), partial
- *         sums in dQaccum (attn_bwd_kernels then names
- *         fused_partial_sum_kernel): their rows add two fp32 halves before
- *         rounding and may differ from attn_bwd's in the last bit; they are
- *         still the same from run to run.
+ *         query range, dQ of the last query blocks by key range); the
+ *         second half of a unit to finish adds the first's fp32 partial,
+ *         handed over in dQaccum with a counter that attn_bwd_preprocess
+ *         zeroed (attn_bwd_kernels then returns "bwd_fused_kernel:split").
+ *         Those rows add two fp32 halves before rounding and may differ from
+ *         attn_bwd's in the last bit; they are still the same from run to
+ *         run (the addition is commutative).
  *   fp32: attn_bwd, then the convert kernel; dQaccum holds the unscaled
  *         sums afterwards, as with attn_bwd.
  * dQ must not overlap any other buffer.  Inputs, D (from
@@ -219,8 +224,9 @@ int attn_bwd_with_dq_noalloc(const attn_params* p, const void* Q, const void* K,
  * attn_bwd_with_dq (with_dq = 1) launches for these parameters on the
  * current device, in launch order, separated by '+' (static storage; ""
  * for an empty problem; NULL when the parameters are invalid or with_dq is
- * not 0 or 1).  Enqueues nothing.  For tests and tools that need to know
- * which path a shape takes.
+ * not 0 or 1).  A name may carry a ":split" suffix: the combined launch
+ * with split work units (see attn_bwd_with_dq).  Enqueues nothing.  For
+ * tests and tools that need to know which path a shape takes.
  */
 const char* attn_bwd_kernels(const attn_params* p, int with_dq);
 

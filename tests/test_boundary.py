@@ -270,17 +270,19 @@ def test_bwd_kernels_query(lib):
     assert plan(1, 4, 4, 512, 128, fab.ATTN_BF16, 1, with_dq=0) == b"bwd_fused_kernel"
     # Given dQ, a combined launch whose heaviest causal units outweigh the
     # per-compute-unit average splits them; balanced grids do not.
-    split = b"bwd_fused_kernel+fused_partial_sum_kernel"
+    split = b"bwd_fused_kernel:split"
     assert plan(1, 1, 1, 16384, 128, fab.ATTN_BF16, 1) == split
     assert plan(1, 1, 1, 16384, 128, fab.ATTN_BF16, 1, with_dq=0) == b"bwd_fused_kernel"
     assert plan(1, 2, 1, 3000, 128, fab.ATTN_BF16, 1) == split
     assert plan(1, 1, 1, 16384, 128, fab.ATTN_BF16, 0) == b"bwd_fused_kernel"         # equal units
     assert plan(2, 16, 16, 1024, 64, fab.ATTN_BF16, 1) == b"bwd_fused_kernel"         # 2 units per compute unit
+    assert plan(1, 16, 16, 1024, 128, fab.ATTN_BF16, 1) == b"bwd_fused_kernel"        # packing: too little to gain
+    assert plan(2, 4, 4, 2500, 128, fab.ATTN_BF16, 1) == b"bwd_fused_kernel"          # packing: too little to gain
+    assert plan(1, 4, 4, 2048, 128, fab.ATTN_BF16, 1) == split
     # The combined launch takes up to 2048 workgroups at d = 64, 1024 at d = 128.
     assert plan(8, 8, 8, 2048, 64, fab.ATTN_BF16, 1, with_dq=0) == b"bwd_fused_kernel"
     assert plan(8, 16, 16, 2048, 64, fab.ATTN_BF16, 1, with_dq=0) == b"bwd_dkdv_kernel+bwd_dq_kernel"
     assert plan(4, 16, 16, 2048, 128, fab.ATTN_BF16, 1, with_dq=0) == b"bwd_dkdv_kernel+bwd_dq_kernel"
-    assert plan(1, 16, 16, 1024, 128, fab.ATTN_BF16, 1) == b"bwd_fused_kernel"        # too little to gain
     assert plan(1, 8, 8, 16384, 128, fab.ATTN_BF16, 1) == b"bwd_dkdv_kernel+bwd_dq_kernel"
     # Grouped heads with few units: the dK/dV work is split over two workgroups
     # per unit; given dQ the dQ kernel adds the partials, else a sum launch.
