@@ -104,20 +104,27 @@ def _check_kernel_stubs(lib: str) -> None:
         raise RuntimeError("kernel launch stubs missing from libfabwd.so: " + ", ".join(missing))
 
 
-PROBE_SRC = os.path.join(PKG, "probes", "dq_update_probe.cpp")
-PROBE_BIN = os.path.join(BUILD, "dq_update_probe")
+PROBES = {
+    "dq_update_probe": os.path.join(PKG, "probes", "dq_update_probe.cpp"),
+    "issue_mix_probe": os.path.join(PKG, "probes", "issue_mix_probe.hip"),
+}
 
 
-def build_probe() -> str:
-    """Builds the standalone dQ-update traffic probe (probes/dq_update_probe.cpp)
-    into _build/dq_update_probe; run it directly (or under rocprofv3)."""
+def build_probe() -> list:
+    """Builds the standalone measurement probes (probes/: the dQ-update traffic
+    probe and the issue-mix probe) into _build/<name>; run them directly (or
+    under rocprofv3).  Returns the binaries' paths."""
     os.makedirs(BUILD, exist_ok=True)
-    cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", PROBE_SRC, "-o", PROBE_BIN]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"build of the dQ-update probe failed:\n{r.stdout}{r.stderr}")
-    return PROBE_BIN
+    out = []
+    for name, src in PROBES.items():
+        exe = os.path.join(BUILD, name)
+        cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", src, "-o", exe]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"build of {name} failed:\n{r.stdout}{r.stderr}")
+        out.append(exe)
+    return out
 
 
 if __name__ == "__main__":
