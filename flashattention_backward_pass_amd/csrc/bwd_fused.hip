@@ -49,15 +49,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     int H_kv, int N,
     int BH_kv, int BH_q, float scale, float softcap, int wl, int wr, Dropout drop, unsigned n_dkdv, unsigned n_dq,
     int qblocks, int qq) {
-  // Blocks 0 .. 2m-1 alternate between the two kinds (m = the smaller
-  // count); the rest belong to the larger kind.
-  const unsigned m = min(n_dkdv, n_dq);
+  // Blocks 0 .. 2m-1 interleave the two kinds (m = the smaller count) in
+  // runs of 8: blocks 16g .. 16g+7 take dK/dV units 8g .. 8g+7, blocks
+  // 16g+8 .. 16g+15 dQ units 8g .. 8g+7.  The hardware places block b on XCD
+  // b % 8, so every XCD gets both kinds, and unit u of either kind lands on
+  // XCD u % 8: a key/value head's dK/dV and dQ units share an XCD and its L2.
+  // Past the last full run the kinds alternate; the rest of the blocks
+  // belong to the larger kind.
+  const unsigned m = min(n_dkdv, n_dq), m8 = m & ~7u;
   const unsigned b = blockIdx.x;
   bool dq_unit;
   unsigned unit;
-  if (b < 2 * m) {
-    dq_unit = (b & 1u) != 0;
-    unit = b >> 1;
+  if (b < 2 * m8) {
+    dq_unit = ((b >> 3) & 1u) != 0;
+    unit = ((b >> 4) << 3) | (b & 7u);
+  } else if (b < 2 * m) {
+    dq_unit = ((b - 2 * m8) & 1u) != 0;
+    unit = m8 + ((b - 2 * m8) >> 1);
   } else {
     dq_unit = n_dq > n_dkdv;
     unit = b - m;
@@ -195,8 +203,14 @@ int64_t fused_makespan(const Problem& p, int a, int c) {
     }
     heap[k] = v;
   };
-  const int64_t m = std::min(n1, n2);
-  for (int64_t u = 0; u < m; ++u) {
+  // The dispatch order of bwd_fused_kernel: runs of 8 of each kind, then
+  // alternating, then the rest of the larger kind.
+  const int64_t m = std::min(n1, n2), m8 = m & ~int64_t(7);
+  for (int64_t u0 = 0; u0 < m8; u0 += 8) {
+    for (int64_t u = u0; u < u0 + 8; ++u) place(kv_weight(u));
+    for (int64_t u = u0; u < u0 + 8; ++u) place(q_weight(u));
+  }
+  for (int64_t u = m8; u < m; ++u) {
     place(kv_weight(u));
     place(q_weight(u));
   }
